@@ -1,2 +1,17 @@
-"""DiT attention hot path for MI355X (gfx950): thin Python binding over the
-C-ABI library ``libdit_attn.so``.  See ``include/dit_attn.h`` for the calls."""
+"""DiT attention hot path for MI355X (gfx950).
+
+Thin Python binding over the C-ABI library ``libdit_attn.so`` (declared in
+``include/dit_attn.h``).  Calls raise if the library is not built; there is no
+CPU fallback.
+"""
+
+from .binding import (  # noqa: F401
+    DitError,
+    attn_block_fwd,
+    attn_lse_merge,
+    attn_patch_fwd,
+    cfg_combine,
+    default_scale,
+    load,
+    status_string,
+)

@@ -1,0 +1,167 @@
+// C ABI of libdit_attn: argument validation and dispatch.
+//
+// Every check runs before any HIP runtime call, so a rejected call touches
+// neither the device nor the stream (and the checks can be exercised on a
+// machine without a GPU).  Accepted calls enqueue their kernels on the
+// caller's stream and return without synchronising.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/dit_attn.h"
+#include "launch.h"
+
+namespace {
+
+constexpr long long kMaxI32 = 0x7fffffffLL;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+bool dtype_ok(int t) { return t == DIT_F32 || t == DIT_BF16; }
+size_t elt_size(dit_dtype_t t) { return t == DIT_BF16 ? 2 : 4; }
+bool head_dim_ok(int d) { return d >= 8 && d <= 128 && d % 8 == 0; }
+
+dit_status_t from_hip(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_HIP; }
+
+// Shared checks of the attention calls; fills the byte sizes of each tensor.
+dit_status_t check_attn(const void* Q, const void* K, const void* V, const void* O,
+                        const float* LSE, int B, int H, int Nq, int Nkv, int d, float scale,
+                        int in_dtype, int out_dtype, size_t* q_bytes, size_t* kv_bytes,
+                        size_t* o_bytes, size_t* l_bytes) {
+  if (!Q || !K || !V || !O || !LSE) return DIT_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nkv <= 0 || d <= 0) return DIT_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return DIT_ERR_INVALID_ARG;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return DIT_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return DIT_ERR_INVALID_ARG;
+  if (!head_dim_ok(d)) return DIT_ERR_UNSUPPORTED;
+  if (in_dtype == DIT_F32 && out_dtype != DIT_F32) return DIT_ERR_UNSUPPORTED;
+  const long long bh = (long long)B * H;
+  // Work items (query tiles of 64 rows at the finest) must fit a 1-D grid.
+  if (bh > kMaxI32 || bh * ((Nq + 63) / 64) > kMaxI32) return DIT_ERR_UNSUPPORTED;
+  const size_t ie = elt_size((dit_dtype_t)in_dtype), oe = elt_size((dit_dtype_t)out_dtype);
+  *q_bytes = (size_t)bh * Nq * d * ie;
+  *kv_bytes = (size_t)bh * Nkv * d * ie;
+  *o_bytes = (size_t)bh * Nq * d * oe;
+  *l_bytes = (size_t)bh * Nq * sizeof(float);
+  return DIT_OK;
+}
+
+bool outputs_clash(const void* O, size_t ob, const float* L, size_t lb, const void* const* ins,
+                   const size_t* in_bytes, int n_in) {
+  if (overlaps(O, ob, L, lb)) return true;
+  for (int i = 0; i < n_in; ++i)
+    if (overlaps(O, ob, ins[i], in_bytes[i]) || overlaps(L, lb, ins[i], in_bytes[i])) return true;
+  return false;
+}
+
+dit_status_t run_attn(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH,
+                      int Nq, int Nkv, int d, float scale, int in_dtype, int out_dtype,
+                      hipStream_t stream) {
+  if (in_dtype == DIT_BF16)
+    return from_hip(dit::launch_attn_bf16(Q, K, V, O, LSE, BH, Nq, Nkv, d, scale,
+                                          out_dtype == DIT_F32, stream));
+  return from_hip(dit::launch_attn_f32(static_cast<const float*>(Q), static_cast<const float*>(K),
+                                       static_cast<const float*>(V), static_cast<float*>(O), LSE,
+                                       BH, Nq, Nkv, d, scale, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+dit_status_t attn_block_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int B, int H, int Nq, int Nkv, int d, float scale,
+                            dit_dtype_t in_dtype, dit_dtype_t out_dtype, hipStream_t stream) {
+  size_t qb, kvb, ob, lb;
+  const dit_status_t st = check_attn(Q, K, V, O, LSE, B, H, Nq, Nkv, d, scale, (int)in_dtype,
+                                     (int)out_dtype, &qb, &kvb, &ob, &lb);
+  if (st != DIT_OK) return st;
+  const void* ins[3] = {Q, K, V};
+  const size_t inb[3] = {qb, kvb, kvb};
+  if (outputs_clash(O, ob, LSE, lb, ins, inb, 3)) return DIT_ERR_INVALID_ARG;
+  return run_attn(Q, K, V, O, LSE, B * H, Nq, Nkv, d, scale, in_dtype, out_dtype, stream);
+}
+
+dit_status_t attn_lse_merge(void* O_a, float* LSE_a, const void* O_b, const float* LSE_b,
+                            long long rows, int d, dit_dtype_t o_dtype, hipStream_t stream) {
+  if (!O_a || !LSE_a || !O_b || !LSE_b) return DIT_ERR_INVALID_ARG;
+  if (rows <= 0 || d <= 0) return DIT_ERR_INVALID_ARG;
+  if (!dtype_ok((int)o_dtype)) return DIT_ERR_INVALID_ARG;
+  if (!aligned16(O_a) || !aligned16(LSE_a) || !aligned16(O_b) || !aligned16(LSE_b))
+    return DIT_ERR_INVALID_ARG;
+  if (!head_dim_ok(d)) return DIT_ERR_UNSUPPORTED;
+  if (rows > (kMaxI32 * 4LL)) return DIT_ERR_UNSUPPORTED;
+  const size_t ob = (size_t)rows * d * elt_size(o_dtype), lb = (size_t)rows * sizeof(float);
+  const bool same_o = O_a == O_b, same_l = LSE_a == LSE_b;
+  if (same_o != same_l) return DIT_ERR_INVALID_ARG;          // half-aliased pair
+  if (!same_o && (overlaps(O_a, ob, O_b, ob) || overlaps(LSE_a, lb, LSE_b, lb)))
+    return DIT_ERR_INVALID_ARG;
+  if (overlaps(O_a, ob, LSE_a, lb) || overlaps(O_a, ob, LSE_b, lb) || overlaps(O_b, ob, LSE_a, lb))
+    return DIT_ERR_INVALID_ARG;
+  return from_hip(dit::launch_lse_merge(O_a, LSE_a, O_b, LSE_b, rows, d, o_dtype == DIT_BF16, stream));
+}
+
+dit_status_t attn_patch_fwd(const void* Q_p, const void* K_p, const void* V_p, void* K_buf,
+                            void* V_buf, void* O, float* LSE, int B, int H, int Np, int N, int p0,
+                            int d, float scale, dit_dtype_t in_dtype, dit_dtype_t out_dtype,
+                            hipStream_t stream) {
+  if (!K_p || !V_p || !K_buf || !V_buf) return DIT_ERR_INVALID_ARG;
+  if (N <= 0 || Np <= 0 || p0 < 0 || (long long)p0 + Np > N) return DIT_ERR_INVALID_ARG;
+  size_t qb, kvb, ob, lb;
+  const dit_status_t st = check_attn(Q_p, K_buf, V_buf, O, LSE, B, H, Np, N, d, scale,
+                                     (int)in_dtype, (int)out_dtype, &qb, &kvb, &ob, &lb);
+  if (st != DIT_OK) return st;
+  if (!aligned16(K_p) || !aligned16(V_p)) return DIT_ERR_INVALID_ARG;
+  const size_t pb = qb;  // fresh K/V patches have the query patch's shape
+  if (overlaps(K_buf, kvb, V_buf, kvb)) return DIT_ERR_INVALID_ARG;
+  const void* bufs[2] = {K_buf, V_buf};
+  const void* fresh[3] = {Q_p, K_p, V_p};
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(bufs[i], kvb, fresh[j], pb)) return DIT_ERR_INVALID_ARG;
+  const void* ins[5] = {Q_p, K_p, V_p, K_buf, V_buf};
+  const size_t inb[5] = {pb, pb, pb, kvb, kvb};
+  if (outputs_clash(O, ob, LSE, lb, ins, inb, 5)) return DIT_ERR_INVALID_ARG;
+
+  const long long row_units = (long long)d * (long long)elt_size(in_dtype) / 16;
+  hipError_t e = dit::launch_splice2(K_p, K_buf, V_p, V_buf, B * H, (long long)Np * row_units,
+                                     (long long)N * row_units, (long long)p0 * row_units, stream);
+  if (e != hipSuccess) return DIT_ERR_HIP;
+  return run_attn(Q_p, K_buf, V_buf, O, LSE, B * H, Np, N, d, scale, in_dtype, out_dtype, stream);
+}
+
+dit_status_t cfg_combine(const float* eps_u, const float* eps_c, float* out, long long n, float s,
+                         hipStream_t stream) {
+  if (!eps_u || !eps_c || !out) return DIT_ERR_INVALID_ARG;
+  if (n <= 0 || !isfinite(s)) return DIT_ERR_INVALID_ARG;
+  if (!aligned16(eps_u) || !aligned16(eps_c) || !aligned16(out)) return DIT_ERR_INVALID_ARG;
+  const size_t nb = (size_t)n * sizeof(float);
+  if (out != eps_u && overlaps(out, nb, eps_u, nb)) return DIT_ERR_INVALID_ARG;
+  if (out != eps_c && overlaps(out, nb, eps_c, nb)) return DIT_ERR_INVALID_ARG;
+  return from_hip(dit::launch_cfg(eps_u, eps_c, out, n, s, stream));
+}
+
+const char* dit_status_string(dit_status_t status) {
+  switch (status) {
+    case DIT_OK:
+      return "DIT_OK: success";
+    case DIT_ERR_INVALID_ARG:
+      return "DIT_ERR_INVALID_ARG: invalid argument (null, non-positive size, misaligned or "
+             "overlapping buffer, bad scale, patch out of range or unknown dtype)";
+    case DIT_ERR_UNSUPPORTED:
+      return "DIT_ERR_UNSUPPORTED: valid but unsupported (head dim, dtype pairing or size)";
+    case DIT_ERR_HIP:
+      return "DIT_ERR_HIP: the HIP kernel launch failed";
+  }
+  return "unknown dit_status_t value";
+}
+
+}  // extern "C"

@@ -1,0 +1,312 @@
+"""Benchmark of the DiT per-device attention step on one MI355X.
+
+One step = one pass of the whole hot path over synthetic DiT-shaped inputs
+that are resident in HBM before timing starts:
+
+  1. sequence-parallel (Ring/Torus) share at 2048 px: B1 H24 d128, a 2048-token
+     query block against 8 KV blocks of 2048 tokens -> 8 attn_block_fwd calls
+     (fp32 partials) folded by 7 attn_lse_merge calls;
+  2. PipeFusion share of a video DiT: B1 H24 d128, 8192 patch queries at token
+     offset 8192 against a 32768-row KV buffer of fresh and stale blocks ->
+     one attn_patch_fwd call (splice + attention);
+  3. classifier-free guidance on two [2, 4, 32, 32] fp32 noise predictions,
+     s = 4 -> one cfg_combine call.
+
+Prints ONE JSON line.  `value` is attention TFLOP/s over the whole step
+(4*B*H*Nq*Nkv*d flops per attention call, divided by the step's wall time,
+merges, splice and CFG included).  Per-phase times, the roofline of the
+dominant kernel and the fp64 CPU oracle on a bounded sample ride along.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s and % of bf16 MFMA peak; merge/CFG GB/s % of HBM peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "attn_fwd_bf16_d128_video_patch_traffic.txt")
+ATTN_SRC = os.path.join(ROOT, "attention_attn_block_amd", "csrc", "attn_bf16.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-supplementary", action="store_true")
+    return ap.parse_args()
+
+
+def attn_flops(B, H, Nq, Nkv, d):
+    return 4.0 * B * H * Nq * Nkv * d
+
+
+def kernel_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None if that summary was taken on other kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", txt)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_b:
+        return None
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+def cpu_baseline(w_patch):
+    """fp64 oracle on a bounded sample of the dominant phase: all 24 heads of
+    the PipeFusion patch attention, 768 query rows each, over the full
+    32768-row buffer (the splice is a copy and is left out)."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    from tests.gpu_util import to_oracle
+
+    rows = np.arange(0, 8192, 8192 // 768)[:768]
+    q, kb, vb = to_oracle(w_patch["q_p"]), to_oracle(w_patch["k_buf"]), to_oracle(w_patch["v_buf"])
+    B, H, _, d = q.shape
+    N = kb.shape[2]
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    oracle.ref_attn(q, kb, vb, w_patch["scale"], rows=rows)
+    dt = time.perf_counter() - t0
+    flops = attn_flops(B, H, rows.size, N, d)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle attention, B{B} H{H}, {rows.size} of 8192 patch query rows "
+                      f"against the full {N}-row buffer, d{d}: {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    rank = int(os.environ.get("RANK", "0"))
+    if args.gpus != 1 or world != 1:
+        if rank == 0:
+            print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+                  "(sharding across devices is described, not built). Use --gpus 1.",
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attention_attn_block_amd import (attn_block_fwd, attn_lse_merge, attn_patch_fwd,
+                                          cfg_combine, inputs, load)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, resident in HBM -------------------------------------------------
+    wr = inputs.ring_2048px()
+    wp = inputs.video_patch()
+    wc = inputs.dit_xl_256()
+    q_r = wr["q"].to(dev)
+    ks = [k.to(dev) for k in wr["ks"]]
+    vs = [v.to(dev) for v in wr["vs"]]
+    Br, Hr, Nqr, dr = q_r.shape
+    Nkr = ks[0].shape[2]
+    o_acc = torch.empty((Br, Hr, Nqr, dr), dtype=torch.float32, device=dev)
+    l_acc = torch.empty((Br, Hr, Nqr), dtype=torch.float32, device=dev)
+    o_cur, l_cur = torch.empty_like(o_acc), torch.empty_like(l_acc)
+    q_p, k_p, v_p = (wp[n].to(dev) for n in ("q_p", "k_p", "v_p"))
+    k_buf, v_buf = wp["k_buf"].to(dev), wp["v_buf"].to(dev)
+    p0 = wp["p0"]
+    Bp, Hp, Np, dp = q_p.shape
+    Nb = k_buf.shape[2]
+    o_p = torch.empty((Bp, Hp, Np, dp), dtype=torch.bfloat16, device=dev)
+    l_p = torch.empty((Bp, Hp, Np), dtype=torch.float32, device=dev)
+    eps_u, eps_c = wc["eps_u"].to(dev), wc["eps_c"].to(dev)
+    eps_out = torch.empty_like(eps_u)
+    s_cfg = wc["s"]
+    nblk = len(ks)
+
+    f_ring = nblk * attn_flops(Br, Hr, Nqr, Nkr, dr)
+    f_patch = attn_flops(Bp, Hp, Np, Nb, dp)
+    f_step = f_ring + f_patch
+    merge_bytes = 3 * o_acc.numel() * 4 + 3 * l_acc.numel() * 4     # read a, b; write a
+    splice_bytes = 2 * 2 * k_p.numel() * 2                           # K and V, read + write
+    cfg_bytes = 3 * eps_u.numel() * 4
+
+    n_ev = 2 * nblk + 2 * (nblk - 1) + 4
+
+    def step(ev=None):
+        i = 0
+
+        def rec():
+            nonlocal i
+            if ev is not None:
+                ev[i].record()
+                i += 1
+
+        for j in range(nblk):
+            tgt_o, tgt_l = (o_acc, l_acc) if j == 0 else (o_cur, l_cur)
+            rec()
+            attn_block_fwd(q_r, ks[j], vs[j], scale=wr["scale"], out_dtype=torch.float32,
+                           out=tgt_o, lse=tgt_l)
+            rec()
+            if j:
+                rec()
+                attn_lse_merge(o_acc, l_acc, o_cur, l_cur)
+                rec()
+        rec()
+        attn_patch_fwd(q_p, k_p, v_p, k_buf, v_buf, p0, scale=wp["scale"], out=o_p, lse=l_p)
+        rec()
+        rec()
+        cfg_combine(eps_u, eps_c, s_cfg, out=eps_out)
+        rec()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region ------------------------------------------------------------
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    ring_ms, merge_ms, patch_ms, cfg_ms = [], [], [], []
+    for ev in evs:
+        i = 0
+        for j in range(nblk):
+            ring_ms.append(ev[i].elapsed_time(ev[i + 1]))
+            i += 2
+            if j:
+                merge_ms.append(ev[i].elapsed_time(ev[i + 1]))
+                i += 2
+        patch_ms.append(ev[i].elapsed_time(ev[i + 1]))
+        i += 2
+        cfg_ms.append(ev[i].elapsed_time(ev[i + 1]))
+
+    def mean(x):
+        return sum(x) / len(x)
+
+    ring_us, merge_us, patch_us, cfg_us = (1e3 * mean(x) for x in (ring_ms, merge_ms, patch_ms, cfg_ms))
+    f_block = attn_flops(Br, Hr, Nqr, Nkr, dr)
+    patch_tflops = f_patch / (patch_us * 1e-6) / 1e12
+    phases = {
+        "ring_block_attn": {"us_per_call": ring_us, "calls_per_step": nblk,
+                            "tflops": f_block / (ring_us * 1e-6) / 1e12,
+                            "frac_bf16_peak": f_block / (ring_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS},
+        "lse_merge_in_sequence": {"us_per_call": merge_us, "calls_per_step": nblk - 1,
+                                  "gbs": merge_bytes / (merge_us * 1e-6) / 1e9,
+                                  "frac_hbm_peak": merge_bytes / (merge_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                  "note": "cache-warm: O_b was just written by the block call"},
+        "patch_splice_plus_attn": {"us_per_call": patch_us, "tflops": patch_tflops,
+                                   "frac_bf16_peak": patch_tflops / PEAK_BF16_TFLOPS},
+        "cfg_combine": {"us_per_call": cfg_us, "gbs": cfg_bytes / (cfg_us * 1e-6) / 1e9,
+                        "note": "96 KiB working set: launch-latency bound"},
+    }
+
+    # ---- supplementary, outside the timed region ---------------------------------
+    supp = {}
+    if not args.no_supplementary:
+        supp = supplementary(torch, dev, attn_block_fwd, attn_lse_merge, cfg_combine, inputs)
+
+    roofline = {"bound": "mfma", "achieved": patch_tflops, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": patch_tflops / PEAK_BF16_TFLOPS,
+                "traffic": kernel_traffic(),
+                "kernel": "attn_fwd_bf16_kernel<128, bf16 out> in attn_patch_fwd "
+                          "(8192 queries x 32768 keys x 24 heads; timed with the splice "
+                          "that precedes it in the same call)"}
+
+    value = f_step / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dit_device_step: ring share B1 H24 d128 2048q x 8x2048kv "
+                               "(8 block fwd fp32 partials + 7 LSE merges) + PipeFusion share "
+                               "B1 H24 d128 8192 patch q x 32768-row fresh/stale KV buffer "
+                               "(splice + attention) + CFG combine 2x4x32x32 fp32 s=4",
+                   "attn_flops_per_step": f_step, "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
+        "roofline": roofline,
+        "phases": phases,
+        "supplementary": supp,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wp)
+    print(json.dumps(out), flush=True)
+
+
+def supplementary(torch, dev, attn_block_fwd, attn_lse_merge, cfg_combine, inputs):
+    """Reported beside the step: merge and CFG on cold HBM (rotating buffers
+    larger than the 256 MB Infinity Cache), and the d=72 workloads."""
+    res = {}
+
+    def timed(fn, iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(iters):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters   # us
+
+    # LSE merge, ring-share shape (49152 rows x d128 fp32), 8 rotating sets (608 MB).
+    rows, d = 24 * 2048, 128
+    sets = [(torch.randn(rows, d, device=dev), torch.randn(rows, device=dev),
+             torch.randn(rows, d, device=dev), torch.randn(rows, device=dev)) for _ in range(8)]
+    fn = lambda i: attn_lse_merge(*sets[i % 8])
+    for i in range(8):
+        fn(i)
+    us = timed(fn, 64)
+    nbytes = 3 * rows * d * 4 + 3 * rows * 4
+    res["lse_merge_cold_d128_f32"] = {"us": us, "gbs": nbytes / us / 1e3,
+                                      "frac_hbm_peak": nbytes / us / 1e3 / PEAK_HBM_GBS,
+                                      "bytes": nbytes}
+    del sets
+
+    # CFG combine at 2^26 floats per tensor (768 MB per call).
+    n = 1 << 26
+    u, c, o = (torch.randn(n, device=dev) for _ in range(3))
+    fn = lambda i: cfg_combine(u, c, 4.0, out=o)
+    fn(0)
+    us = timed(fn, 20)
+    nbytes = 3 * n * 4
+    res["cfg_combine_2^26"] = {"us": us, "gbs": nbytes / us / 1e3,
+                               "frac_hbm_peak": nbytes / us / 1e3 / PEAK_HBM_GBS}
+    del u, c, o
+
+    # d = 72 attention: PixArt-style 1024 px and DiT-XL/2 256 px.
+    for name in ("pixart_1024", "dit_xl_256"):
+        w = inputs.make(name)
+        q, k, v = (w[x].to(dev) for x in ("q", "k", "v"))
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        fn = lambda i: attn_block_fwd(q, k, v, scale=w["scale"], out=out, lse=lse)
+        for i in range(3):
+            fn(i)
+        us = timed(fn, 20)
+        B, H, Nq, dd = q.shape
+        tf = attn_flops(B, H, Nq, k.shape[2], dd) / (us * 1e-6) / 1e12
+        res[f"attn_{name}"] = {"us": us, "tflops": tf, "frac_bf16_peak": tf / PEAK_BF16_TFLOPS}
+    return res
+
+
+if __name__ == "__main__":
+    main()

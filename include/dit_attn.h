@@ -1,0 +1,156 @@
+/*
+ * dit_attn -- the per-device attention step of parallel DiT inference on one
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The calls follow the problem as the pages state it:
+ *  - attention over image-patch tokens is where DiT inference spends its time
+ *    ("xDiT: an Inference Engine for Diffusion Transformers (DiTs) with
+ *    Massive Parallelism", abstract);
+ *  - sequence parallelism hands each device its queries plus a series of KV
+ *    blocks whose partial results must be combined -- Ring attention passes
+ *    the blocks between neighbours and Torus attention starts on each chunk as
+ *    it arrives ("SwiftFusion: Scalable Sequence Parallelism for Distributed
+ *    Inference of Diffusion Transformers on GPUs", sections 1 and 2);
+ *  - PipeFusion, the patch-level pipeline, has a device attend its patch's
+ *    queries to the whole image's KV (xDiT abstract), and Orchestra gives
+ *    devices patches of unequal size ("Spatio-Temporal Parallelism for
+ *    Diffusion Model Inference on Heterogeneous Multi-GPU Systems", abstract);
+ *  - CFG parallelism runs the conditional and unconditional paths apart and
+ *    only their noise predictions meet ("Accelerating Diffusion via Hybrid
+ *    Data-Pipeline Parallelism Based on Conditional Guidance Scheduling",
+ *    Technische Zusammenfassung, 2.A).
+ * No page writes a formula; each call below states the textbook definition it
+ * computes.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer is a device pointer owned by the caller and must be 16-byte
+ *    aligned.  The library allocates no memory, keeps no per-call state and
+ *    needs no workspace.
+ *  - Work is enqueued on `stream` (0 = the null stream) and returns without
+ *    synchronising.  Calls on different streams may run concurrently.
+ *  - Tensors are row-major and contiguous: [B, H, N, d] with d innermost;
+ *    log-sum-exp arrays are [B, H, N] float32.
+ *  - Supported head dims: d a multiple of 8 with 8 <= d <= 128.
+ *  - Element types: DIT_BF16 (bfloat16) or DIT_F32 (float32).  bfloat16
+ *    inputs may produce bfloat16 or float32 outputs; float32 inputs produce
+ *    float32 outputs.  Arithmetic is float32 throughout (bfloat16 matrix-core
+ *    products accumulate in float32).
+ *  - All argument checks run before any HIP call; a rejected call touches
+ *    neither the device nor the stream.  Return codes:
+ *      DIT_OK               enqueued;
+ *      DIT_ERR_INVALID_ARG  null pointer, non-positive size, misaligned or
+ *                           overlapping buffers, bad scale, patch out of range,
+ *                           unknown dtype value;
+ *      DIT_ERR_UNSUPPORTED  valid but not implemented (d, dtype pairing, sizes
+ *                           beyond 32-bit indexing);
+ *      DIT_ERR_HIP          the kernel launch failed.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - Log-sum-exp values are natural logarithms.  LSE = -inf marks an empty
+ *    partial result in attn_lse_merge.
+ */
+#ifndef DIT_ATTN_H
+#define DIT_ATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DIT_OK = 0,
+  DIT_ERR_INVALID_ARG = 1,
+  DIT_ERR_UNSUPPORTED = 2,
+  DIT_ERR_HIP = 3
+} dit_status_t;
+
+typedef enum { DIT_F32 = 0, DIT_BF16 = 1 } dit_dtype_t;
+
+/*
+ * Block attention: one query block against one KV block.
+ *
+ *   O[b,h,i,:] = sum_j softmax_j(scale * <Q[b,h,i,:], K[b,h,j,:]>) V[b,h,j,:]
+ *   LSE[b,h,i] = ln sum_j exp(scale * <Q[b,h,i,:], K[b,h,j,:]>)
+ *
+ * This is the unit of work a sequence-parallel device repeats for every KV
+ * block it receives (SwiftFusion, sections 1-2; xDiT abstract).  No mask or
+ * bias: DiT self-attention over patches is bidirectional.
+ *   Q: [B,H,Nq,d] in_dtype;  K, V: [B,H,Nkv,d] in_dtype      (read only)
+ *   O: [B,H,Nq,d] out_dtype; LSE: [B,H,Nq] float32          (written)
+ *   B, H, Nq, Nkv >= 1;  scale > 0 and finite (usually 1/sqrt(d)).
+ * O and LSE must not overlap Q, K, V or each other.
+ */
+dit_status_t attn_block_fwd(const void* Q, const void* K, const void* V,
+                            void* O, float* LSE,
+                            int B, int H, int Nq, int Nkv, int d, float scale,
+                            dit_dtype_t in_dtype, dit_dtype_t out_dtype,
+                            hipStream_t stream);
+
+/*
+ * Log-sum-exp merge of two partials over disjoint key sets, in place into a.
+ *
+ * Per row r (rows = B*H*Nq):
+ *   LSE_b = -inf           : a unchanged (an empty partial is the identity),
+ *                            except that two empty partials give O_a <- 0
+ *   LSE_a = -inf           : a <- b
+ *   otherwise m = max(LSE_a, LSE_b), w_a = e^(LSE_a-m), w_b = e^(LSE_b-m),
+ *             O_a <- (w_a O_a + w_b O_b) / (w_a + w_b),
+ *             LSE_a <- m + ln(w_a + w_b).
+ * This folds the result of each arriving KV block into a device's running
+ * output (SwiftFusion, sections 1-2).
+ *   O_a: [rows, d] o_dtype, LSE_a: [rows] float32     (read and written)
+ *   O_b: [rows, d] o_dtype, LSE_b: [rows] float32     (read only)
+ *   rows >= 1.  b may equal a exactly (O_b == O_a and LSE_b == LSE_a);
+ *   any other overlap between a and b is rejected.
+ */
+dit_status_t attn_lse_merge(void* O_a, float* LSE_a,
+                            const void* O_b, const float* LSE_b,
+                            long long rows, int d, dit_dtype_t o_dtype,
+                            hipStream_t stream);
+
+/*
+ * PipeFusion patch step: splice the fresh patch into the device's KV buffer,
+ * then attend the patch queries to the whole buffer.
+ *
+ *   K_buf[b,h,p0+i,:] <- K_p[b,h,i,:],  V_buf[b,h,p0+i,:] <- V_p[b,h,i,:]
+ *                                                  for 0 <= i < Np (bit copy)
+ *   (O, LSE) <- attn_block_fwd(Q_p, K_buf, V_buf) over all N buffer rows.
+ * Rows of the buffer outside [p0, p0+Np) keep whatever the caller left there
+ * (stale KV from the previous denoising step) (xDiT abstract).  Any Np >= 1
+ * at any offset is accepted, so devices may hold patches of unequal size
+ * (Orchestra, abstract).
+ *   Q_p, K_p, V_p: [B,H,Np,d] in_dtype       (read only)
+ *   K_buf, V_buf:  [B,H,N,d] in_dtype        (rows [p0,p0+Np) overwritten)
+ *   O: [B,H,Np,d] out_dtype; LSE: [B,H,Np] float32   (written)
+ *   1 <= Np, 0 <= p0, p0 + Np <= N;  scale > 0 and finite.
+ * The fresh patch must not overlap the buffers; O and LSE must overlap
+ * nothing else.
+ */
+dit_status_t attn_patch_fwd(const void* Q_p, const void* K_p, const void* V_p,
+                            void* K_buf, void* V_buf,
+                            void* O, float* LSE,
+                            int B, int H, int Np, int N, int p0, int d, float scale,
+                            dit_dtype_t in_dtype, dit_dtype_t out_dtype,
+                            hipStream_t stream);
+
+/*
+ * Classifier-free guidance combine of the unconditional and conditional
+ * noise predictions (Hybridiff, Technische Zusammenfassung, 2.A):
+ *   out[i] = eps_u[i] + s * (eps_c[i] - eps_u[i]),
+ * evaluated in fp32 as fma(s, eps_c[i], (1 - s) * eps_u[i]) so that s = 1
+ * returns eps_c and s = 0 returns eps_u bit for bit (finite inputs).
+ *   eps_u, eps_c, out: [n] float32, n >= 1, s finite.
+ *   out may be exactly eps_u or exactly eps_c; no other overlap.
+ */
+dit_status_t cfg_combine(const float* eps_u, const float* eps_c, float* out,
+                         long long n, float s, hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* dit_status_string(dit_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_ATTN_H */

@@ -1,0 +1,185 @@
+"""CPU tests of the C ABI: the library loads, exports every declared call, and
+rejects bad arguments before any HIP call (no GPU needed: a call that reached
+the HIP runtime here would return DIT_ERR_HIP, not the validation code)."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from attention_attn_block_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dit_attn.h")
+
+OK, INV, UNS, HIP = 0, 1, 2, 3
+F32, BF16 = 0, 1
+
+# Fake, 16-byte aligned, widely spaced device addresses: validation only looks
+# at their values.
+BASE = 0x7F0000000000
+GAP = 1 << 36
+
+
+def ptr(i, off=0):
+    return BASE + i * GAP + off
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_status_strings(lib):
+    for code in (OK, INV, UNS, HIP):
+        s = binding.status_string(code)
+        assert s.startswith(["DIT_OK", "DIT_ERR_INVALID_ARG", "DIT_ERR_UNSUPPORTED", "DIT_ERR_HIP"][code])
+    assert "unknown" in binding.status_string(17)
+
+
+# ---------------------------------------------------------------------------
+# attn_block_fwd
+# ---------------------------------------------------------------------------
+
+def block(lib, **kw):
+    a = dict(Q=ptr(0), K=ptr(1), V=ptr(2), O=ptr(3), LSE=ptr(4), B=1, H=2, Nq=100, Nkv=70, d=64,
+             scale=0.125, i=BF16, o=BF16)
+    a.update(kw)
+    return lib.attn_block_fwd(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["Nq"],
+                              a["Nkv"], a["d"], a["scale"], a["i"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), INV), (dict(K=None), INV), (dict(V=None), INV), (dict(O=None), INV),
+    (dict(LSE=None), INV),
+    (dict(B=0), INV), (dict(H=-1), INV), (dict(Nq=0), INV), (dict(Nkv=0), INV), (dict(d=0), INV),
+    (dict(scale=0.0), INV), (dict(scale=-1.0), INV), (dict(scale=math.nan), INV),
+    (dict(scale=math.inf), INV),
+    (dict(i=7), INV), (dict(o=-1), INV),
+    (dict(Q=ptr(0, 2)), INV), (dict(K=ptr(1, 8)), INV), (dict(O=ptr(3, 4)), INV),
+    (dict(LSE=ptr(4, 4)), INV),
+    (dict(d=60), UNS), (dict(d=136), UNS), (dict(d=4), UNS),
+    (dict(i=F32, o=BF16), UNS),
+    (dict(B=1 << 20, H=1 << 12), UNS),
+    (dict(O=ptr(0, 64)), INV),                   # O overlaps Q
+    (dict(LSE=ptr(3, 256)), INV),                # LSE overlaps O
+    (dict(O=ptr(1)), INV),                       # O aliases K
+])
+def test_attn_block_fwd_rejects(lib, kw, code):
+    assert block(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# attn_lse_merge
+# ---------------------------------------------------------------------------
+
+def merge(lib, **kw):
+    a = dict(Oa=ptr(0), La=ptr(1), Ob=ptr(2), Lb=ptr(3), rows=1000, d=128, t=F32)
+    a.update(kw)
+    return lib.attn_lse_merge(a["Oa"], a["La"], a["Ob"], a["Lb"], a["rows"], a["d"], a["t"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Oa=None), INV), (dict(La=None), INV), (dict(Ob=None), INV), (dict(Lb=None), INV),
+    (dict(rows=0), INV), (dict(rows=-5), INV), (dict(d=0), INV), (dict(t=3), INV),
+    (dict(Oa=ptr(0, 4)), INV), (dict(Lb=ptr(3, 8)), INV),
+    (dict(d=12), UNS), (dict(d=256), UNS),
+    (dict(Ob=ptr(0)), INV),                      # O aliased but LSE not
+    (dict(Ob=ptr(0, 512)), INV),                 # partial overlap of O
+    (dict(Lb=ptr(1, 16)), INV),                  # partial overlap of LSE
+    (dict(La=ptr(0, 1024)), INV),                # LSE_a inside O_a
+])
+def test_attn_lse_merge_rejects(lib, kw, code):
+    assert merge(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# attn_patch_fwd
+# ---------------------------------------------------------------------------
+
+def patch(lib, **kw):
+    a = dict(Q=ptr(0), Kp=ptr(1), Vp=ptr(2), Kb=ptr(3), Vb=ptr(4), O=ptr(5), L=ptr(6), B=1, H=4,
+             Np=64, N=256, p0=64, d=128, scale=0.088, i=BF16, o=BF16)
+    a.update(kw)
+    return lib.attn_patch_fwd(a["Q"], a["Kp"], a["Vp"], a["Kb"], a["Vb"], a["O"], a["L"], a["B"],
+                              a["H"], a["Np"], a["N"], a["p0"], a["d"], a["scale"], a["i"], a["o"],
+                              None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), INV), (dict(Kp=None), INV), (dict(Vp=None), INV), (dict(Kb=None), INV),
+    (dict(Vb=None), INV), (dict(O=None), INV), (dict(L=None), INV),
+    (dict(p0=-1), INV), (dict(p0=200), INV), (dict(Np=257), INV), (dict(Np=0), INV),
+    (dict(N=0), INV), (dict(scale=0.0), INV),
+    (dict(Kp=ptr(1, 2)), INV), (dict(Vb=ptr(4, 8)), INV),
+    (dict(d=100), UNS), (dict(i=F32, o=BF16), UNS),
+    (dict(Kp=ptr(3, 4096)), INV),                # fresh patch inside the buffer
+    (dict(Vb=ptr(3, 1 << 16)), INV),             # K and V buffers overlap
+    (dict(O=ptr(4, 128)), INV),                  # output inside V buffer
+])
+def test_attn_patch_fwd_rejects(lib, kw, code):
+    assert patch(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# cfg_combine
+# ---------------------------------------------------------------------------
+
+def cfg(lib, **kw):
+    a = dict(u=ptr(0), c=ptr(1), o=ptr(2), n=8192, s=4.0)
+    a.update(kw)
+    return lib.cfg_combine(a["u"], a["c"], a["o"], a["n"], a["s"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), INV), (dict(c=None), INV), (dict(o=None), INV), (dict(n=0), INV),
+    (dict(n=-3), INV), (dict(s=math.nan), INV), (dict(s=-math.inf), INV),
+    (dict(u=ptr(0, 4)), INV), (dict(o=ptr(2, 8)), INV),
+    (dict(o=ptr(0, 16)), INV),                   # out partially overlaps eps_u
+    (dict(o=ptr(1, 32)), INV),                   # out partially overlaps eps_c
+])
+def test_cfg_combine_rejects(lib, kw, code):
+    assert cfg(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# Python binding: marshalling checks that never reach the library
+# ---------------------------------------------------------------------------
+
+def test_binding_rejects_host_tensors():
+    q = torch.zeros(1, 1, 4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.attn_block_fwd(q, q, q)
+    with pytest.raises(ValueError):
+        binding.cfg_combine(torch.zeros(4), torch.zeros(4), 1.0)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load()

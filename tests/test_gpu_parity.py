@@ -1,0 +1,285 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Small and medium cases compare every output element; the full-size
+PipeFusion workload compares sampled query rows (the oracle computes them
+one by one) plus the whole spliced buffer bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_attn_block_amd import (attn_block_fwd, attn_lse_merge, attn_patch_fwd,
+                                      cfg_combine, inputs)
+from tests.gpu_util import (assert_bf16_close, assert_close, assert_f32_close, to_f64,
+                            to_oracle)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU (no fallback)"
+    torch.cuda.init()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(t):
+    return t.to("cuda:0")
+
+
+def run_attn(q, k, v, scale, out_dtype):
+    O, L = attn_block_fwd(dev(q), dev(k), dev(v), scale=scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return O, L
+
+
+def check_attn(q, k, v, scale, out_dtype, what):
+    say("case", what, tuple(q.shape), tuple(k.shape), out_dtype)
+    O, L = run_attn(q, k, v, scale, out_dtype)
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale)
+    fp32 = q.dtype == torch.float32
+    assert_close(to_f64(O), Or, fp32, what + " O")
+    assert_close(to_f64(L), Lr, fp32, what + " LSE")
+    return O, L
+
+
+# ---------------------------------------------------------------------------
+# Workloads at their stated sizes
+# ---------------------------------------------------------------------------
+
+def test_tiny_f32_full_and_four_block_merge():
+    w = inputs.tiny_f32()
+    q, k, v, scale = w["q"], w["k"], w["v"], w["scale"]
+    check_attn(q, k, v, scale, torch.float32, "tiny_f32 full")
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale)
+    nb = w["blocks"]
+    step = k.shape[2] // nb
+    say("case tiny_f32 4-block fold")
+    acc_o, acc_l = None, None
+    for j in range(nb):
+        Oj, Lj = run_attn(q, k[:, :, j * step:(j + 1) * step].contiguous(),
+                          v[:, :, j * step:(j + 1) * step].contiguous(), scale, torch.float32)
+        if acc_o is None:
+            acc_o, acc_l = Oj, Lj
+        else:
+            attn_lse_merge(acc_o, acc_l, Oj, Lj)
+    torch.cuda.synchronize()
+    assert_f32_close(to_f64(acc_o), Or, "fold O")
+    assert_f32_close(to_f64(acc_l), Lr, "fold LSE")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_dit_xl_256_attention(out_dtype):
+    w = inputs.dit_xl_256()
+    check_attn(w["q"], w["k"], w["v"], w["scale"], out_dtype, "dit_xl_256")
+
+
+def test_dit_xl_256_cfg():
+    w = inputs.dit_xl_256()
+    say("case dit_xl_256 cfg")
+    out = cfg_combine(dev(w["eps_u"]), dev(w["eps_c"]), w["s"])
+    torch.cuda.synchronize()
+    ref = oracle.ref_cfg(to_oracle(w["eps_u"]), to_oracle(w["eps_c"]), w["s"])
+    assert_f32_close(to_f64(out), ref, "cfg")
+
+
+def test_pixart_1024_attention():
+    w = inputs.pixart_1024()
+    check_attn(w["q"], w["k"], w["v"], w["scale"], torch.bfloat16, "pixart_1024")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_ring_2048px_eight_blocks_merged(out_dtype):
+    """8 sequential block calls folded with 7 merges equal attention over all
+    16384 keys.  fp32 partials are the default reading; bf16 partials are
+    checked too, against the same tolerances."""
+    w = inputs.ring_2048px()
+    q = dev(w["q"])
+    acc_o = acc_l = None
+    say("case ring_2048px", out_dtype)
+    for kj, vj in zip(w["ks"], w["vs"]):
+        Oj, Lj = attn_block_fwd(q, dev(kj), dev(vj), scale=w["scale"], out_dtype=out_dtype)
+        if acc_o is None:
+            acc_o, acc_l = Oj, Lj
+        else:
+            attn_lse_merge(acc_o, acc_l, Oj, Lj)
+    torch.cuda.synchronize()
+    K = torch.cat(w["ks"], dim=2)
+    V = torch.cat(w["vs"], dim=2)
+    Or, Lr = oracle.ref_attn(to_oracle(w["q"]), to_oracle(K), to_oracle(V), w["scale"])
+    assert_bf16_close(to_f64(acc_o), Or, "ring O")
+    assert_bf16_close(to_f64(acc_l), Lr, "ring LSE")
+
+
+def test_video_patch_full_size_sampled_rows():
+    w = inputs.video_patch()
+    p0 = w["p0"]
+    Np = w["q_p"].shape[2]
+    say("case video_patch full size", tuple(w["k_buf"].shape))
+    kb, vb = dev(w["k_buf"]), dev(w["v_buf"])
+    kb0, vb0 = kb.clone(), vb.clone()
+    O, L = attn_patch_fwd(dev(w["q_p"]), dev(w["k_p"]), dev(w["v_p"]), kb, vb, p0,
+                          scale=w["scale"])
+    torch.cuda.synchronize()
+    # the spliced buffer, bit for bit
+    kp, vp = dev(w["k_p"]), dev(w["v_p"])
+    assert torch.equal(kb[:, :, p0:p0 + Np], kp) and torch.equal(vb[:, :, p0:p0 + Np], vp)
+    assert torch.equal(kb[:, :, :p0], kb0[:, :, :p0]) and torch.equal(kb[:, :, p0 + Np:], kb0[:, :, p0 + Np:])
+    assert torch.equal(vb[:, :, :p0], vb0[:, :, :p0]) and torch.equal(vb[:, :, p0 + Np:], vb0[:, :, p0 + Np:])
+    del kb0, vb0
+    rng = np.random.default_rng(55)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, Np - 1], rng.choice(Np, 160, replace=False)]))
+    Or, Lr, Kn, _ = oracle.ref_patch(to_oracle(w["q_p"]), to_oracle(w["k_p"]), to_oracle(w["v_p"]),
+                                     to_oracle(w["k_buf"]), to_oracle(w["v_buf"]), p0, w["scale"],
+                                     rows=rows)
+    assert np.array_equal(to_oracle(kb.cpu()), Kn), "spliced K buffer differs from the oracle's"
+    assert_bf16_close(to_f64(O[:, :, rows]), Or, "video_patch O (sampled rows)")
+    assert_bf16_close(to_f64(L[:, :, rows]), Lr, "video_patch LSE (sampled rows)")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases: ragged tiles, odd head dims, tiny and degenerate sizes
+# ---------------------------------------------------------------------------
+
+SHAPES = [
+    # (B, H, Nq, Nkv, d)
+    (1, 1, 1, 1, 64),
+    (1, 2, 63, 257, 64),
+    (2, 1, 257, 63, 72),
+    (1, 1, 1000, 1000, 128),
+    (1, 3, 129, 65, 128),
+    (1, 1, 5, 300, 8),
+    (1, 2, 200, 130, 40),
+    (1, 1, 130, 100, 96),
+    (1, 1, 64, 64, 120),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("in_dtype,out_dtype", [
+    (torch.bfloat16, torch.bfloat16), (torch.bfloat16, torch.float32), (torch.float32, torch.float32)])
+def test_edge_shapes(shape, in_dtype, out_dtype):
+    B, H, Nq, Nkv, d = shape
+    q, k, v = inputs.attn_inputs(B, H, Nq, Nkv, d, "bf16" if in_dtype == torch.bfloat16 else "f32",
+                                 seed=100 + Nq + Nkv + d)
+    check_attn(q, k, v, inputs.default_scale(d), out_dtype, f"edge {shape}")
+
+
+def test_large_scores_stay_finite():
+    """Scores of several hundred (peaked softmax) must not overflow."""
+    q, k, v = inputs.attn_inputs(1, 2, 100, 300, 64, "bf16", seed=7)
+    q = (q.float() * 8).to(torch.bfloat16)
+    k = (k.float() * 8).to(torch.bfloat16)
+    check_attn(q, k, v, 0.125, torch.float32, "peaked scores")
+
+
+def test_merge_edge_cases():
+    rows, d = 300, 72
+    g = torch.Generator().manual_seed(9)
+    for dt in (torch.float32, torch.bfloat16):
+        say("case merge edges", dt)
+        Oa = torch.randn(rows, d, generator=g).to(dt)
+        Ob = torch.randn(rows, d, generator=g).to(dt)
+        La = torch.randn(rows, generator=g) * 3
+        Lb = torch.randn(rows, generator=g) * 3
+        La[::7] = -torch.inf          # empty a
+        Lb[::5] = -torch.inf          # empty b
+        Ob[::5] = torch.nan           # garbage in an empty partial must not leak
+        ga, gla = dev(Oa), dev(La)
+        attn_lse_merge(ga, gla, dev(Ob), dev(Lb))
+        torch.cuda.synchronize()
+        Or, Lr = oracle.ref_lse_merge(to_oracle(Oa), to_oracle(La), to_oracle(Ob), to_oracle(Lb))
+        both_empty = np.isneginf(Lr)
+        got_o, got_l = to_f64(ga), to_f64(gla)
+        assert np.array_equal(np.isneginf(got_l), both_empty)
+        assert np.all(got_o[both_empty] == 0.0), "two empty partials must give O = 0"
+        fin = ~both_empty
+        if dt == torch.float32:
+            assert_f32_close(got_o[fin], Or[fin], "merge O")
+            assert_f32_close(got_l[fin], Lr[fin], "merge LSE")
+        else:
+            assert_bf16_close(got_o[fin], Or[fin], "merge O bf16")
+            assert_bf16_close(got_l[fin], Lr[fin], "merge LSE bf16")
+        # rows where b is empty keep a bit for bit
+        keep = np.isneginf(to_f64(Lb)) & ~np.isneginf(to_f64(La))
+        assert np.array_equal(to_oracle(ga.cpu())[keep], to_oracle(Oa)[keep])
+
+
+def test_merge_in_place_alias():
+    """b == a exactly: O unchanged (to rounding), LSE + ln 2."""
+    g = torch.Generator().manual_seed(10)
+    Oa = torch.randn(500, 128, generator=g)
+    La = torch.randn(500, generator=g)
+    ga, gla = dev(Oa), dev(La)
+    say("case merge alias")
+    attn_lse_merge(ga, gla, ga, gla)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.ref_lse_merge(to_oracle(Oa), to_oracle(La), to_oracle(Oa), to_oracle(La))
+    assert_f32_close(to_f64(ga), Or, "alias O")
+    assert_f32_close(to_f64(gla), Lr, "alias LSE")
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1000, 8192, (1 << 20) + 3])
+def test_cfg_sizes(n):
+    g = torch.Generator().manual_seed(n)
+    u, c = torch.randn(n, generator=g), torch.randn(n, generator=g)
+    say("case cfg n =", n)
+    out = cfg_combine(dev(u), dev(c), 4.0)
+    gu = dev(u)
+    cfg_combine(gu, dev(c), 1.0, out=gu)          # in place into eps_u, s = 1 gives eps_c
+    torch.cuda.synchronize()
+    assert_f32_close(to_f64(out), oracle.ref_cfg(to_oracle(u), to_oracle(c), 4.0), "cfg")
+    assert torch.equal(gu.cpu(), c), "s = 1 must return eps_c exactly"
+
+
+@pytest.mark.parametrize("p", [0, 1, 2, 3])
+def test_patch_each_position_small(p):
+    """4 patches of a shrunk video buffer (same recipe), every position, ragged patch."""
+    N, Np, H = 4 * 300, 300, 3
+    w = inputs.video_patch(p0=p * Np, N=N, Np=Np, H=H)
+    say("case patch position", p)
+    kb, vb = dev(w["k_buf"]), dev(w["v_buf"])
+    O, L = attn_patch_fwd(dev(w["q_p"]), dev(w["k_p"]), dev(w["v_p"]), kb, vb, w["p0"],
+                          scale=w["scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Or, Lr, Kn, Vn = oracle.ref_patch(to_oracle(w["q_p"]), to_oracle(w["k_p"]), to_oracle(w["v_p"]),
+                                      to_oracle(w["k_buf"]), to_oracle(w["v_buf"]), w["p0"],
+                                      w["scale"])
+    assert np.array_equal(to_oracle(kb.cpu()), Kn) and np.array_equal(to_oracle(vb.cpu()), Vn)
+    assert_bf16_close(to_f64(O), Or, "patch O")
+    assert_bf16_close(to_f64(L), Lr, "patch LSE")
+
+
+@pytest.mark.parametrize("Np,p0,N", [(1, 0, 50), (1, 49, 50), (50, 0, 50), (17, 33, 50)])
+def test_patch_degenerate(Np, p0, N):
+    w = inputs.video_patch(p0=p0, N=N, Np=Np, H=2)
+    say("case patch degenerate", Np, p0, N)
+    kb, vb = dev(w["k_buf"]), dev(w["v_buf"])
+    O, L = attn_patch_fwd(dev(w["q_p"]), dev(w["k_p"]), dev(w["v_p"]), kb, vb, p0, scale=w["scale"])
+    torch.cuda.synchronize()
+    Or, Lr, Kn, _ = oracle.ref_patch(to_oracle(w["q_p"]), to_oracle(w["k_p"]), to_oracle(w["v_p"]),
+                                     to_oracle(w["k_buf"]), to_oracle(w["v_buf"]), p0, w["scale"])
+    assert np.array_equal(to_oracle(kb.cpu()), Kn)
+    assert_bf16_close(to_f64(O), Or, "patch O")
+    assert_bf16_close(to_f64(L), Lr, "patch LSE")
+
+
+def test_deterministic_and_stream_ordered():
+    """Two runs give identical bits (no LDS races); a side stream orders correctly."""
+    q, k, v = inputs.attn_inputs(2, 4, 700, 900, 128, "bf16", seed=3)
+    q, k, v = dev(q), dev(k), dev(v)
+    say("case determinism")
+    O1, L1 = attn_block_fwd(q, k, v)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        O2, L2 = attn_block_fwd(q, k, v)
+        O2 = O2.clone()
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
