@@ -32,11 +32,14 @@
 //    L2 for the head's K/V stream.
 // Scores are kept in the log2 domain (scale * log2 e folded into one FMA) and
 // exponentiated with v_exp_f32; the LSE is converted back to natural log.
-// P is rounded to bfloat16 (RNE, v_cvt_pk_bf16_f32) for the PV product; the
-// normaliser is summed from the fp32 values.
+// P is rounded to bfloat16 (RNE, v_cvt_pk_bf16_f32) for the PV product and
+// the normaliser sums those same bf16 weights (v_dot2_f32_bf16 against ones),
+// so the output is an exactly normalised combination of the values.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "launch.h"
 
@@ -45,6 +48,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -53,7 +57,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kBr = 128;        // query rows per workgroup
 constexpr int kBc = 64;         // keys per KV tile
-constexpr int kVs = kBc + 8;    // transposed-V LDS row stride (elements)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -65,11 +68,8 @@ struct Geo {
   static constexpr int kOct = D / 8;                // 16-byte groups per row in memory
   static constexpr int kKs = kChunks * 16 + 8;      // K LDS row stride (elements)
   static constexpr int kKElems = kBc * kKs;
-  static constexpr int kVElems = kDTiles * 32 * kVs;
-  static constexpr int kKItems = kBc * kOct;        // 16-byte K groups per tile
+  static constexpr int kKItems = kBc * kOct;        // 16-byte K (or V) groups per tile
   static constexpr int kKLoads = (kKItems + kThreads - 1) / kThreads;
-  static constexpr int kVItems = (kBc / 4) * kOct;  // (key quad, 16-byte group) items per V tile
-  static constexpr int kVLoads = (kVItems + kThreads - 1) / kThreads;
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -98,23 +98,36 @@ __device__ __forceinline__ float sum_with_partner32(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Position of key k (0..63 within a tile) in the transposed-V row.  Inside
-// each 16-key chunk the accumulator of S^T gives lanes 0-31 keys
-// {0-3, 8-11} and lanes 32-63 keys {4-7, 12-15}; the B operand of the PV
-// product takes 8 consecutive slots per half-wave, so key quads 1 and 2 of
-// every chunk swap places.
-__device__ __forceinline__ int vt_quad_pos(int kq) {
-  const int c = kq >> 2, q = kq & 3;
-  return 16 * c + 4 * (((q & 1) << 1) | (q >> 1));
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i names a row of 4 consecutive bf16; lane i then receives element
+// (i % 4) of the rows named by lanes 4k + i/4, k = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
 }
+
+// Row stride (elements) of the row-major V tile in LDS.  A row must hold the
+// 32 * kDTiles columns the transposing reads touch; the stride is chosen
+// congruent to 64 or 192 bytes modulo 256 so that the four 64-byte row pieces
+// one half-wave reads fall in distinct banks.
+constexpr int v_stride(int dtiles) { return dtiles == 1 ? 32 : dtiles <= 3 ? 96 : 160; }
+
+// Rescale threshold (log2 units): the running maximum used for the
+// exponentials is only moved when a row's score maximum exceeds it by more
+// than this, so most tiles skip rescaling the output accumulator.  Weights
+// stay below 2^8 and the result is unchanged in exact arithmetic.
+constexpr float kTau = 8.f;
 
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     void* __restrict__ Out, float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, float c2) {
   using G = Geo<D>;
+  constexpr int kVsr = v_stride(G::kDTiles);
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][G::kKElems];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][G::kVElems];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kBc * kVsr];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,82 +164,81 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     }
   }
 
+  // K and V tiles are staged through registers: 16-byte groups, row-major.
+  // Lane-constant parts of the global and LDS addresses are computed once.
+  constexpr bool kFullLoads = (G::kKItems % kThreads) == 0;
   u32x4 kreg[G::kKLoads];
-  u32x4 vreg[G::kVLoads][4];
+  u32x4 vreg[G::kKLoads];
+  int g_off[G::kKLoads];     // element offset of this lane's group inside a tile
+  int g_key[G::kKLoads];     // key of that group inside the tile
+  int ks_off[G::kKLoads];    // LDS element offsets (K, V)
+  int vs_off[G::kKLoads];
+#pragma unroll
+  for (int j = 0; j < G::kKLoads; ++j) {
+    const int i = tid + kThreads * j;
+    const int key = i / G::kOct, oc = i - key * G::kOct;
+    g_key[j] = key;
+    g_off[j] = key * D + 8 * oc;
+    ks_off[j] = key * G::kKs + 8 * oc;
+    vs_off[j] = key * kVsr + 8 * oc;
+  }
+  auto active = [&](int j) { return kFullLoads || tid + kThreads * j < G::kKItems; };
 
   auto load_tile = [&](int kv0) {
+    const __bf16* kt = Kh + (size_t)kv0 * D;
+    const __bf16* vt = Vh + (size_t)kv0 * D;
+    if (kv0 + kBc <= Nkv) {
 #pragma unroll
-    for (int j = 0; j < G::kKLoads; ++j) {
-      const int i = tid + kThreads * j;
-      if (i < G::kKItems) {
-        const int key = i / G::kOct, oc = i - key * G::kOct;
-        int row = kv0 + key;
-        row = row < Nkv ? row : Nkv - 1;
-        kreg[j] = *reinterpret_cast<const u32x4*>(Kh + (size_t)row * D + 8 * oc);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < G::kVLoads; ++j) {
-      const int i = tid + kThreads * j;
-      if (i < G::kVItems) {
-        const int kq = i / G::kOct, oc = i - kq * G::kOct;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int row = kv0 + 4 * kq + r;
-          row = row < Nkv ? row : Nkv - 1;
-          vreg[j][r] = *reinterpret_cast<const u32x4*>(Vh + (size_t)row * D + 8 * oc);
+      for (int j = 0; j < G::kKLoads; ++j)
+        if (active(j)) {
+          kreg[j] = *reinterpret_cast<const u32x4*>(kt + g_off[j]);
+          vreg[j] = *reinterpret_cast<const u32x4*>(vt + g_off[j]);
         }
-      }
+    } else {  // ragged last tile: clamp rows to the block (their weights are zeroed)
+#pragma unroll
+      for (int j = 0; j < G::kKLoads; ++j)
+        if (active(j)) {
+          const int over = kv0 + g_key[j] - (Nkv - 1);
+          const int back = over > 0 ? over * D : 0;
+          kreg[j] = *reinterpret_cast<const u32x4*>(kt + g_off[j] - back);
+          vreg[j] = *reinterpret_cast<const u32x4*>(vt + g_off[j] - back);
+        }
     }
   };
 
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < G::kKLoads; ++j) {
-      const int i = tid + kThreads * j;
-      if (i < G::kKItems) {
-        const int key = i / G::kOct, oc = i - key * G::kOct;
-        *reinterpret_cast<u32x4*>(&k_lds[buf][key * G::kKs + 8 * oc]) = kreg[j];
+    for (int j = 0; j < G::kKLoads; ++j)
+      if (active(j)) {
+        *reinterpret_cast<u32x4*>(&k_lds[buf][ks_off[j]]) = kreg[j];
+        *reinterpret_cast<u32x4*>(&v_lds[buf][vs_off[j]]) = vreg[j];
       }
-    }
-#pragma unroll
-    for (int j = 0; j < G::kVLoads; ++j) {
-      const int i = tid + kThreads * j;
-      if (i < G::kVItems) {
-        const int kq = i / G::kOct, oc = i - kq * G::kOct;
-        const int pos = vt_quad_pos(kq);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          u32x2 pk;
-          if ((e & 1) == 0) {
-            pk.x = (vreg[j][0][w] & 0xffffu) | (vreg[j][1][w] << 16);
-            pk.y = (vreg[j][2][w] & 0xffffu) | (vreg[j][3][w] << 16);
-          } else {
-            pk.x = (vreg[j][0][w] >> 16) | (vreg[j][1][w] & 0xffff0000u);
-            pk.y = (vreg[j][2][w] >> 16) | (vreg[j][3][w] & 0xffff0000u);
-          }
-          *reinterpret_cast<u32x2*>(&v_lds[buf][(8 * oc + e) * kVs + pos]) = pk;
-        }
-      }
-    }
   };
+
+  // Per-lane part of the transposing V reads (see lds_read_tr16): lane group
+  // g = lane / 16 reads keys 4 (g / 2) + (lane % 16) / 4 of each 8-key half
+  // chunk, columns 16 (g % 2) + 4 (lane % 4) of each 32-column d tile.
+  const int vg = lane >> 4, vi = lane & 15;
+  const int v_lane_off = (4 * (vg >> 1) + (vi >> 2)) * kVsr + 16 * (vg & 1) + 4 * (vi & 3);
 
   f32x16 acc[G::kDTiles];
 #pragma unroll
   for (int t = 0; t < G::kDTiles; ++t) acc[t] = f32x16{};
-  float m_run = -INFINITY;  // running row max, log2 units
-  float l_run = 0.f;        // this lane's share of the running normaliser
+  float m_ref = 0.f;   // reference row max for the exponentials, log2 units
+  float l_run = 0.f;   // this lane's share of the running normaliser (bf16 weights)
 
   const int n_tiles = (Nkv + kBc - 1) / kBc;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  // One 64-key tile.  FIRST: the reference max is set from this tile's
+  // maximum.  Later tiles form t = s * c2 - m_ref first (an FMA per score,
+  // needed for the exponent anyway), take the row max of t, and only move the
+  // reference when some row's max exceeds it by kTau.
+  auto tile_step = [&](auto buf_c, auto first_c, int t, bool has_next) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr bool first = decltype(first_c)::value;
     const int kv0 = t * kBc;
-    if (t + 1 < n_tiles) load_tile(kv0 + kBc);
+    if (has_next) load_tile(kv0 + kBc);
 
     // S^T = K Q^T for 64 keys (two 32-key accumulators).
     f32x16 s[2];
@@ -256,49 +268,88 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         }
     }
 
-    float mx = s[0][0];
+    if constexpr (first) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = max_with_partner32(mx);
-    const float m_new = fmaxf(m_run, mx * c2);
-    const float alpha = fast_exp2(m_run - m_new);
-    const float neg_m = -m_new;
-
-    float psum = 0.f;
+        for (int r = 0; r < 16; ++r) s[kt][r] *= c2;
+      float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      m_ref = max_with_partner32(mx);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[kt][r], c2, neg_m));
-        s[kt][r] = p;
-        psum += p;
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] -= m_ref;
+    } else {
+      const float neg_m = -m_ref;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = fmaf(s[kt][r], c2, neg_m);
+      float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+      mx = max_with_partner32(mx);
+      const bool grow = mx > kTau;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float delta = grow ? mx : 0.f;
+        const float alpha = fast_exp2(-delta);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        m_ref += delta;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kt][r] -= delta;
       }
-    l_run = fmaf(l_run, alpha, psum);
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < G::kDTiles; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
 
-    // O^T += V^T P^T, 16 keys per product.
+    // O^T += V^T P^T, 16 keys per product.  Slot j of half-wave h holds key
+    // 8 (j / 4) + 4 h + j % 4 of the chunk on both operands.  The normaliser
+    // sums the same bf16 weights the product uses.
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
       bf16x8 pb;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[ch >> 1][8 * (ch & 1) + j];
+      for (int j = 0; j < 8; ++j) pb[j] = (__bf16)fast_exp2(s[ch >> 1][8 * (ch & 1) + j]);
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0], pb[1]}, ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2], pb[3]}, ones, ls1, false);
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[4], pb[5]}, ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[6], pb[7]}, ones, ls1, false);
 #pragma unroll
       for (int dt = 0; dt < G::kDTiles; ++dt) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&v_lds[buf][(dt * 32 + l32) * kVs + 16 * ch + 8 * hi]);
+        const __bf16* vp = &v_lds[buf][v_lane_off + 16 * ch * kVsr + 32 * dt];
+        const bf16x4 lo = lds_read_tr16(vp);
+        const bf16x4 up = lds_read_tr16(vp + 8 * kVsr);
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
         acc[dt] = mfma32(a, pb, acc[dt]);
       }
     }
+    l_run += ls0 + ls1;
 
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    if (has_next) store_tile(buf ^ 1);
     __syncthreads();
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using First = std::true_type;
+  using Later = std::false_type;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  tile_step(I0{}, First{}, 0, n_tiles > 1);
+  int t = 1;
+  for (; t + 2 <= n_tiles; t += 2) {
+    tile_step(I1{}, Later{}, t, true);
+    tile_step(I0{}, Later{}, t + 1, t + 2 < n_tiles);
   }
+  if (t < n_tiles) tile_step(I1{}, Later{}, t, false);
 
   const float l_tot = sum_with_partner32(l_run);
   if (my_q < Nq) {
@@ -320,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
           }
         }
       }
-    if (hi == 0) LSE[(size_t)bh * Nq + my_q] = (m_run + fast_log2(l_tot)) * kLn2;
+    if (hi == 0) LSE[(size_t)bh * Nq + my_q] = (m_ref + fast_log2(l_tot)) * kLn2;
   }
 }
 
