@@ -8,9 +8,11 @@ CPU fallback.
 from .binding import (  # noqa: F401
     DitError,
     attn_block_fwd,
+    attn_block_fwd_merge,
     attn_lse_merge,
     attn_patch_fwd,
     cfg_combine,
+    cfg_combine_relmae,
     default_scale,
     load,
     status_string,

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libdit_attn.so")
 DIT_OK, DIT_ERR_INVALID_ARG, DIT_ERR_UNSUPPORTED, DIT_ERR_HIP = 0, 1, 2, 3
 DIT_F32, DIT_BF16 = 0, 1
 
-EXPORTS = ("attn_block_fwd", "attn_lse_merge", "attn_patch_fwd", "cfg_combine",
+EXPORTS = ("attn_block_fwd", "attn_block_fwd_merge", "attn_lse_merge", "attn_patch_fwd",
+           "cfg_combine", "cfg_combine_relmae", "cfg_combine_relmae_workspace",
            "dit_status_string")
 
 _lib = None
@@ -41,10 +42,15 @@ def load():
     L = ctypes.CDLL(LIB_PATH)
     vp, i, ll, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float
     L.attn_block_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    L.attn_block_fwd_merge.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     L.attn_lse_merge.argtypes = [vp, vp, vp, vp, ll, i, i, vp]
     L.attn_patch_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     L.cfg_combine.argtypes = [vp, vp, vp, ll, f, vp]
-    for name in ("attn_block_fwd", "attn_lse_merge", "attn_patch_fwd", "cfg_combine"):
+    L.cfg_combine_relmae.argtypes = [vp, vp, vp, ll, f, vp, vp, vp]
+    L.cfg_combine_relmae_workspace.argtypes = [ll]
+    L.cfg_combine_relmae_workspace.restype = ll
+    for name in ("attn_block_fwd", "attn_block_fwd_merge", "attn_lse_merge", "attn_patch_fwd",
+                 "cfg_combine", "cfg_combine_relmae"):
         getattr(L, name).restype = ctypes.c_int
     L.dit_status_string.argtypes = [ctypes.c_int]
     L.dit_status_string.restype = ctypes.c_char_p
@@ -115,6 +121,26 @@ def attn_block_fwd(q, k, v, scale=None, out_dtype=None, out=None, lse=None):
     return out, lse
 
 
+def attn_block_fwd_merge(q, k, v, o_acc, lse_acc, scale=None):
+    """Fold the attention of q against this KV block into (o_acc, lse_acc) in
+    place; rows with lse_acc = -inf are empty and take the block's result."""
+    dev = _dev(q, k, v, o_acc, lse_acc)
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if k.shape != (B, H, Nkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v shapes/dtypes disagree")
+    if o_acc.shape != (B, H, Nq, d) or lse_acc.shape != (B, H, Nq) \
+            or lse_acc.dtype != torch.float32:
+        raise ValueError("o_acc/lse_acc shape or dtype mismatch")
+    scale = default_scale(d) if scale is None else float(scale)
+    with torch.cuda.device(dev):
+        rc = load().attn_block_fwd_merge(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         o_acc.data_ptr(), lse_acc.data_ptr(), B, H, Nq, Nkv, d,
+                                         scale, _dtype(q.dtype), _dtype(o_acc.dtype), _stream(dev))
+    _check("attn_block_fwd_merge", rc)
+    return o_acc, lse_acc
+
+
 def attn_lse_merge(o_a, lse_a, o_b, lse_b):
     """In place: (o_a, lse_a) <- merge of a and b.  o_*: [..., d], lse_*: [...]."""
     dev = _dev(o_a, lse_a, o_b, lse_b)
@@ -175,3 +201,29 @@ def cfg_combine(eps_u, eps_c, s, out=None):
                                 eps_u.numel(), float(s), _stream(dev))
     _check("cfg_combine", rc)
     return out
+
+
+def cfg_combine_relmae(eps_u, eps_c, s, out=None, workspace=None, relmae=None):
+    """(out, relmae) with out = eps_u + s (eps_c - eps_u) and relmae =
+    sum|eps_c - eps_u| / sum|eps_u| as a one-element float32 device tensor."""
+    dev = _dev(eps_u, eps_c)
+    if eps_u.shape != eps_c.shape or eps_u.dtype != torch.float32 or eps_c.dtype != torch.float32:
+        raise ValueError("eps_u/eps_c must be float32 tensors of one shape")
+    n = eps_u.numel()
+    if out is None:
+        out = torch.empty_like(eps_u)
+    nw = load().cfg_combine_relmae_workspace(n)
+    if workspace is None:
+        workspace = torch.empty(max(nw, 4), dtype=torch.float32, device=dev)
+    if relmae is None:
+        relmae = torch.empty(4, dtype=torch.float32, device=dev)[:1]
+    _dev(eps_u, out, workspace, relmae)
+    if out.shape != eps_u.shape or out.dtype != torch.float32 or workspace.numel() < nw \
+            or workspace.dtype != torch.float32 or relmae.dtype != torch.float32:
+        raise ValueError("out/workspace/relmae shape or dtype mismatch")
+    with torch.cuda.device(dev):
+        rc = load().cfg_combine_relmae(eps_u.data_ptr(), eps_c.data_ptr(), out.data_ptr(), n,
+                                       float(s), workspace.data_ptr(), relmae.data_ptr(),
+                                       _stream(dev))
+    _check("cfg_combine_relmae", rc)
+    return out, relmae

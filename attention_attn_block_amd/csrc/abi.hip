@@ -63,14 +63,14 @@ bool outputs_clash(const void* O, size_t ob, const float* L, size_t lb, const vo
 }
 
 dit_status_t run_attn(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH,
-                      int Nq, int Nkv, int d, float scale, int in_dtype, int out_dtype,
+                      int Nq, int Nkv, int d, float scale, int in_dtype, int out_dtype, bool merge,
                       hipStream_t stream) {
   if (in_dtype == DIT_BF16)
     return from_hip(dit::launch_attn_bf16(Q, K, V, O, LSE, BH, Nq, Nkv, d, scale,
-                                          out_dtype == DIT_F32, stream));
+                                          out_dtype == DIT_F32, merge, stream));
   return from_hip(dit::launch_attn_f32(static_cast<const float*>(Q), static_cast<const float*>(K),
                                        static_cast<const float*>(V), static_cast<float*>(O), LSE,
-                                       BH, Nq, Nkv, d, scale, stream));
+                                       BH, Nq, Nkv, d, scale, merge, stream));
 }
 
 }  // namespace
@@ -87,7 +87,22 @@ dit_status_t attn_block_fwd(const void* Q, const void* K, const void* V, void* O
   const void* ins[3] = {Q, K, V};
   const size_t inb[3] = {qb, kvb, kvb};
   if (outputs_clash(O, ob, LSE, lb, ins, inb, 3)) return DIT_ERR_INVALID_ARG;
-  return run_attn(Q, K, V, O, LSE, B * H, Nq, Nkv, d, scale, in_dtype, out_dtype, stream);
+  return run_attn(Q, K, V, O, LSE, B * H, Nq, Nkv, d, scale, in_dtype, out_dtype, false, stream);
+}
+
+dit_status_t attn_block_fwd_merge(const void* Q, const void* K, const void* V, void* O_acc,
+                                  float* LSE_acc, int B, int H, int Nq, int Nkv, int d,
+                                  float scale, dit_dtype_t in_dtype, dit_dtype_t acc_dtype,
+                                  hipStream_t stream) {
+  size_t qb, kvb, ob, lb;
+  const dit_status_t st = check_attn(Q, K, V, O_acc, LSE_acc, B, H, Nq, Nkv, d, scale,
+                                     (int)in_dtype, (int)acc_dtype, &qb, &kvb, &ob, &lb);
+  if (st != DIT_OK) return st;
+  const void* ins[3] = {Q, K, V};
+  const size_t inb[3] = {qb, kvb, kvb};
+  if (outputs_clash(O_acc, ob, LSE_acc, lb, ins, inb, 3)) return DIT_ERR_INVALID_ARG;
+  return run_attn(Q, K, V, O_acc, LSE_acc, B * H, Nq, Nkv, d, scale, in_dtype, acc_dtype, true,
+                  stream);
 }
 
 dit_status_t attn_lse_merge(void* O_a, float* LSE_a, const void* O_b, const float* LSE_b,
@@ -135,7 +150,8 @@ dit_status_t attn_patch_fwd(const void* Q_p, const void* K_p, const void* V_p, v
   hipError_t e = dit::launch_splice2(K_p, K_buf, V_p, V_buf, B * H, (long long)Np * row_units,
                                      (long long)N * row_units, (long long)p0 * row_units, stream);
   if (e != hipSuccess) return DIT_ERR_HIP;
-  return run_attn(Q_p, K_buf, V_buf, O, LSE, B * H, Np, N, d, scale, in_dtype, out_dtype, stream);
+  return run_attn(Q_p, K_buf, V_buf, O, LSE, B * H, Np, N, d, scale, in_dtype, out_dtype, false,
+                  stream);
 }
 
 dit_status_t cfg_combine(const float* eps_u, const float* eps_c, float* out, long long n, float s,
@@ -147,6 +163,29 @@ dit_status_t cfg_combine(const float* eps_u, const float* eps_c, float* out, lon
   if (out != eps_u && overlaps(out, nb, eps_u, nb)) return DIT_ERR_INVALID_ARG;
   if (out != eps_c && overlaps(out, nb, eps_c, nb)) return DIT_ERR_INVALID_ARG;
   return from_hip(dit::launch_cfg(eps_u, eps_c, out, n, s, stream));
+}
+
+long long cfg_combine_relmae_workspace(long long n) {
+  return n > 0 ? dit::cfg_relmae_work_floats(n) : 0;
+}
+
+dit_status_t cfg_combine_relmae(const float* eps_u, const float* eps_c, float* out, long long n,
+                                float s, float* workspace, float* relmae, hipStream_t stream) {
+  if (!eps_u || !eps_c || !out || !workspace || !relmae) return DIT_ERR_INVALID_ARG;
+  if (n <= 0 || !isfinite(s)) return DIT_ERR_INVALID_ARG;
+  if (!aligned16(eps_u) || !aligned16(eps_c) || !aligned16(out) || !aligned16(workspace) ||
+      !aligned16(relmae))
+    return DIT_ERR_INVALID_ARG;
+  const size_t nb = (size_t)n * sizeof(float);
+  const size_t wb = (size_t)dit::cfg_relmae_work_floats(n) * sizeof(float);
+  if (out != eps_u && overlaps(out, nb, eps_u, nb)) return DIT_ERR_INVALID_ARG;
+  if (out != eps_c && overlaps(out, nb, eps_c, nb)) return DIT_ERR_INVALID_ARG;
+  const void* all[3] = {eps_u, eps_c, out};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(workspace, wb, all[i], nb) || overlaps(relmae, 4, all[i], nb))
+      return DIT_ERR_INVALID_ARG;
+  if (overlaps(workspace, wb, relmae, 4)) return DIT_ERR_INVALID_ARG;
+  return from_hip(dit::launch_cfg_relmae(eps_u, eps_c, out, n, s, workspace, relmae, stream));
 }
 
 const char* dit_status_string(dit_status_t status) {

@@ -1,0 +1,7 @@
+// Explicit instantiations of the bf16 attention launch for head dims 104, 112.
+#include "attn_bf16_kernel.h"
+
+namespace dit {
+template hipError_t launch_bf16_d<104>(const void*, const void*, const void*, void*, float*, int, int, int, float, bool, bool, hipStream_t);
+template hipError_t launch_bf16_d<112>(const void*, const void*, const void*, void*, float*, int, int, int, float, bool, bool, hipStream_t);
+}  // namespace dit

@@ -1,0 +1,483 @@
+// Block attention over bfloat16 Q/K/V on gfx950 matrix cores (kernel template;
+// instantiated per head dim in attn_bf16_d*.hip, dispatched in attn_bf16.hip).
+//
+// Computes O = softmax(Q K^T * scale) V and LSE = ln sum exp(scale Q K^T) for
+// one query block against one KV block -- the unit of work a sequence-
+// parallel DiT device repeats per KV block ("SwiftFusion: Scalable Sequence
+// Parallelism for Distributed Inference of Diffusion Transformers on GPUs",
+// sections 1-2; "xDiT: an Inference Engine for Diffusion Transformers (DiTs)
+// with Massive Parallelism", abstract).  The key loop is the usual one-pass
+// online softmax: a running row maximum and normaliser, with the output
+// rescaled whenever the maximum grows, so each KV tile is read once.
+//
+// Work decomposition (CDNA4, wave64):
+//  * A workgroup owns 128 query rows of one (batch, head); each of its four
+//    waves owns 32 rows for the whole key loop.
+//  * Both contractions run on v_mfma_f32_32x32x16_bf16 in the transposed
+//    form S^T = K Q^T and O^T = V^T P^T.  In the 32x32 accumulator layout a
+//    lane then holds 16 values of ONE query row (column = lane % 32), so the
+//    softmax row max / row sum are in-register reductions plus a single
+//    exchange with lane ^ 32, and P never leaves registers: the S^T
+//    accumulator registers are exactly the B operand of the PV product once
+//    the keys inside each 16-key chunk are visited in the order the
+//    accumulator holds them.
+//  * K and V tiles of 64 keys move from HBM straight into LDS with
+//    global_load_lds_dwordx4 (no staging registers), double-buffered, in
+//    16-byte units swizzled so that both LDS read patterns are bank-conflict
+//    free.  V stays row-major; the PV operand is read with the transposing
+//    ds_read_b64_tr_b16.
+//  * The key loop is software-pipelined with K one tile ahead of V: while the
+//    vector ALU turns tile t's scores into weights, the matrix cores already
+//    compute tile t+1's scores; one barrier per tile.
+//  * Workgroup ids are remapped so that all query tiles of a head run on the
+//    same XCD (ids are dealt round-robin over the 8 XCDs), sharing that XCD's
+//    L2 for the head's K/V stream.
+// Scores are kept in the log2 domain (scale * log2 e folded into one FMA) and
+// exponentiated with v_exp_f32; the LSE is converted back to natural log.
+// P is rounded to bfloat16 (RNE, v_cvt_pk_bf16_f32) for the PV product and
+// the normaliser sums those same bf16 weights (v_dot2_f32_bf16 against ones),
+// so the output is an exactly normalised combination of the values.
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "launch.h"
+
+namespace dit {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kBr = 128;        // query rows per workgroup
+constexpr int kBc = 64;         // keys per KV tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int D>
+struct Geo {
+  static constexpr int kChunks = (D + 15) / 16;     // 16-wide slices of the QK^T contraction
+  static constexpr bool kHalfTail = (D % 16) == 8;  // last slice has 8 real columns
+  static constexpr int kDTiles = (D + 31) / 32;     // 32-row tiles of O^T
+  static constexpr int kOct = D / 8;                // 16-byte groups per row in memory
+  static constexpr int kKItems = kBc * kOct;        // 16-byte K (or V) groups per tile
+  static constexpr int kKLoads = (kKItems + kThreads - 1) / kThreads;
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Value held by lane ^ 32.  v_permlane32_swap(x, x) leaves lanes 0-31 with
+// (x[l], x[l+32]) and lanes 32-63 with (x[l-32], x[l]); callers combine the
+// pair symmetrically, so own and partner value need not be told apart.
+struct Pair {
+  float a, b;
+};
+__device__ __forceinline__ Pair swap32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_with_partner32(float x) {
+  const Pair p = swap32(x);
+  return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float sum_with_partner32(float x) {
+  const Pair p = swap32(x);
+  return p.a + p.b;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i names a row of 4 consecutive bf16; lane i then receives element
+// (i % 4) of the rows named by lanes 4k + i/4, k = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// 16-byte-unit swizzles of the LDS tiles (row = key inside the tile; stored
+// column = global column ^ swz).  Only for power-of-two units per row; other
+// head dims keep plain row-major order.
+//  swz_k: the K operand read has 16 consecutive lanes on 16 consecutive rows
+//         at one column -> spread them over 16 distinct unit slots.
+//  swz_v: a transposing read has 4 consecutive rows x 4 consecutive units per
+//         half-wave -> give each of the 4 rows its own 4-unit slot group.
+template <int kOct>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (kOct == 16) return row & 15;
+  else if constexpr (kOct == 8) return (row >> 1) & 7;
+  else if constexpr (kOct == 4) return (row >> 2) & 3;
+  else if constexpr (kOct == 2) return (row >> 3) & 1;
+  else return 0;
+}
+template <int kOct>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (kOct == 16) return 4 * (row & 3);
+  else if constexpr (kOct == 8) return 4 * ((row >> 1) & 1);
+  else return 0;
+}
+
+// Rescale threshold (log2 units): the running maximum used for the
+// exponentials is only moved when a row's score maximum exceeds it by more
+// than this, so most tiles skip rescaling the output accumulator.  Weights
+// stay below 2^8 and the result is unchanged in exact arithmetic.
+constexpr float kTau = 8.f;
+
+template <int D, bool OUT_F32, bool MERGE>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    void* __restrict__ Out, float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, float c2) {
+  using G = Geo<D>;
+  // K and V tiles: 64 rows of kOct 16-byte units each, unit-swizzled (see
+  // swz_k / swz_v), plus slack for the transposing reads of the last rows.
+  constexpr int kTileUnits = kBc * G::kOct;
+  constexpr int kBufUnits = kTileUnits + 16;
+  __shared__ u32x4 k_lds[2][kBufUnits];
+  __shared__ u32x4 v_lds[2][kBufUnits];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // XCD-aware remap: workgroup ids are dealt round-robin over the 8 XCDs, so
+  // give each XCD a contiguous range of (head, query tile) work items.
+  const int nblk = gridDim.x;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int slot = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+  const int bh = logical / n_qtiles;
+  const int qt = logical - bh * n_qtiles;
+
+  const __bf16* Qh = Q + (size_t)bh * Nq * D;
+  const __bf16* Kh = K + (size_t)bh * Nkv * D;
+  const __bf16* Vh = V + (size_t)bh * Nkv * D;
+
+  const int my_q = qt * kBr + wave * 32 + l32;
+  const int q_ld = my_q < Nq ? my_q : Nq - 1;
+
+  // Q^T as the B operand: lane holds Q[my_q][16c + 8hi .. +7].
+  bf16x8 qf[G::kChunks];
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) {
+    if (G::kHalfTail && c == G::kChunks - 1 && hi) {
+      qf[c] = bf16x8{};
+    } else {
+      qf[c] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)q_ld * D + 16 * c + 8 * hi);
+    }
+  }
+
+  // Tile staging: global -> LDS directly (global_load_lds_dwordx4, no
+  // registers).  Wave w's j-th load writes LDS units 64 (4j + w) .. +63, lane
+  // i the unit 64 (4j + w) + i; the unit stored there is row p / kOct, stored
+  // column p % kOct, which holds global column (p % kOct) ^ swz(row).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int kg_off[G::kKLoads], vg_off[G::kKLoads], g_row[G::kKLoads];
+#pragma unroll
+  for (int j = 0; j < G::kKLoads; ++j) {
+    const int pu = tid + kThreads * j;
+    const int row = pu / G::kOct, col = pu - row * G::kOct;
+    g_row[j] = row;
+    kg_off[j] = row * D + 8 * (col ^ swz_k<G::kOct>(row));
+    vg_off[j] = row * D + 8 * (col ^ swz_v<G::kOct>(row));
+  }
+  auto dma_tile = [&](const __bf16* base, const int* goff, u32x4* lds, int kv0) {
+    const __bf16* tb = base + (size_t)kv0 * D;
+    const bool full = kv0 + kBc <= Nkv;
+#pragma unroll
+    for (int j = 0; j < G::kKLoads; ++j) {
+      const int first_unit = 64 * (4 * j + wv);
+      if (first_unit < kTileUnits) {  // wave-uniform: kTileUnits is a multiple of 64
+        int off = goff[j];
+        if (!full) {  // ragged last tile: clamp rows into the block
+          const int over = kv0 + g_row[j] - (Nkv - 1);
+          off -= over > 0 ? over * D : 0;
+        }
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(tb + off),
+            (__attribute__((address_space(3))) void*)(lds + first_unit), 16, 0, 0);
+      }
+    }
+  };
+  // All of this wave's tile loads have landed in LDS (before a barrier).
+  auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // K operand addresses: row kt*32 + l32, global column 2c + hi.
+  const int sk = swz_k<G::kOct>(l32);
+  int k_unit[G::kChunks];
+#pragma unroll
+  for (int c = 0; c < G::kChunks; ++c) k_unit[c] = l32 * G::kOct + (((2 * c + hi) ^ sk) % G::kOct);
+
+  // S^T = K Q^T for the 64 keys of the K tile in LDS buffer `buf`.
+  auto qk = [&](int buf, f32x16* s) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < G::kChunks; ++c) {
+        bf16x8 a;
+        if (G::kHalfTail && c == G::kChunks - 1 && hi) {
+          a = bf16x8{};
+        } else {
+          a = __builtin_bit_cast(bf16x8, k_lds[buf][kt * 32 * G::kOct + k_unit[c]]);
+        }
+        s[kt] = mfma32(a, qf[c], s[kt]);
+      }
+    }
+  };
+  // Keys past the end of the block (last tile only) get zero weight.
+  auto mask_tail = [&](f32x16* s, int kv0) {
+    if (kv0 + kBc > Nkv) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= Nkv) s[kt][r] = -INFINITY;
+        }
+    }
+  };
+
+  // Transposing V reads (see lds_read_tr16): in lane group g = lane / 16,
+  // lane i names row 4 (g / 2) + i / 4 of each 8-key half chunk and columns
+  // 16 (g % 2) + 4 (i % 4) .. +3 of each 32-column d tile.  The row's swizzle
+  // depends on i / 4 only, so each d tile gets one lane-constant offset.
+  const int vg = lane >> 4, vi = lane & 15;
+  const int v_row = 4 * (vg >> 1) + (vi >> 2);
+  const int sv = swz_v<G::kOct>(v_row);
+  int v_off[G::kDTiles];  // bf16 element offsets inside a V buffer
+#pragma unroll
+  for (int dt = 0; dt < G::kDTiles; ++dt) {
+    const int unit = 4 * dt + 2 * (vg & 1) + ((vi & 3) >> 1);
+    v_off[dt] = (v_row * G::kOct + (unit ^ sv)) * 8 + 4 * (vi & 1);
+  }
+
+  f32x16 acc[G::kDTiles];
+#pragma unroll
+  for (int t = 0; t < G::kDTiles; ++t) acc[t] = f32x16{};
+  float l_run = 0.f;   // this lane's share of the running normaliser (bf16 weights)
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  const int n_tiles = (Nkv + kBc - 1) / kBc;
+
+  // Software pipeline: K runs one tile ahead of V.  While tile t's softmax
+  // runs on the vector ALU, the matrix cores compute S for tile t + 1.  LDS:
+  // K(t) and V(t) live in buffer t % 2.  Iteration t reads K(t+1) and V(t);
+  // its loads of K(t+2) and V(t+1) land in the buffers iteration t-1 freed.
+  dma_tile(Kh, kg_off, k_lds[0], 0);
+  dma_tile(Vh, vg_off, v_lds[0], 0);
+  if (n_tiles > 1) dma_tile(Kh, kg_off, k_lds[1], kBc);
+  dma_wait();
+  __syncthreads();
+
+  f32x16 s_cur[2];
+  qk(0, s_cur);
+  mask_tail(s_cur, 0);
+  // Reference max from tile 0 (later tiles only move it by more than kTau).
+  float m_ref;
+  {
+    float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
+    m_ref = max_with_partner32(mx) * c2;
+  }
+
+  auto iteration = [&](auto buf_c, int t) {
+    constexpr int cur = decltype(buf_c)::value;  // = t % 2
+    constexpr int nxt = cur ^ 1;
+    const bool has1 = t + 1 < n_tiles, has2 = t + 2 < n_tiles;
+    if (has2) dma_tile(Kh, kg_off, k_lds[cur], (t + 2) * kBc);
+    if (has1) dma_tile(Vh, vg_off, v_lds[nxt], (t + 1) * kBc);
+
+    // ---- matrix cores: S for tile t + 1; vector ALU: weights of tile t ----
+    // (Branch-free so the two interleave.  On the last tile the product reads
+    // an allocated, unused K buffer and its result is dropped.)
+    f32x16 s_nxt[2];
+    qk(nxt, s_nxt);
+
+    const float neg_m = -m_ref;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_cur[kt][r] = fmaf(s_cur[kt][r], c2, neg_m);
+    float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
+    bf16x8 pb[4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[ch][j] = (__bf16)fast_exp2(s_cur[ch >> 1][8 * (ch & 1) + j]);
+    mx = max_with_partner32(mx);
+    // Issue order for this block: K-operand LDS reads two products ahead,
+    // then per product one MFMA, the next read and a share of the softmax
+    // VALU work, so the vector ALU runs while the matrix core is busy.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // LDS read
+#pragma unroll
+    for (int i = 0; i < 2 * G::kChunks; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 96 / G::kChunks, 0);  // VALU
+    }
+    const bool grow = mx > kTau;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // Rare: move the reference to this tile's max for the rows that grew
+      // past it, rescale what was accumulated, recompute this tile's weights.
+      const float delta = grow ? mx : 0.f;
+      const float alpha = fast_exp2(-delta);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      m_ref += delta;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const __bf16 re = (__bf16)fast_exp2(s_cur[ch >> 1][8 * (ch & 1) + j] - delta);
+          pb[ch][j] = grow ? re : pb[ch][j];
+        }
+    }
+
+    // ---- O^T += V^T P^T (16 keys per product) and the row sums ----
+    // Slot j of half-wave h holds key 8 (j / 4) + 4 h + j % 4 of the chunk on
+    // both operands.
+    const __bf16* vb = reinterpret_cast<const __bf16*>(v_lds[cur]);
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt) {
+        const __bf16* vp = vb + v_off[dt] + 16 * ch * G::kOct * 8;
+        const bf16x4 lo = lds_read_tr16(vp);
+        const bf16x4 up = lds_read_tr16(vp + 8 * G::kOct * 8);
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+        acc[dt] = mfma32(a, pb[ch], acc[dt]);
+      }
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][0], pb[ch][1]}, ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][2], pb[ch][3]}, ones, ls1, false);
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][4], pb[ch][5]}, ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][6], pb[ch][7]}, ones, ls1, false);
+    }
+    l_run += ls0 + ls1;
+
+    dma_wait();
+    __syncthreads();
+    if (has1) {
+      mask_tail(s_nxt, (t + 1) * kBc);
+      s_cur[0] = s_nxt[0];
+      s_cur[1] = s_nxt[1];
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t + 2 <= n_tiles; t += 2) {
+    iteration(I0{}, t);
+    iteration(I1{}, t + 1);
+  }
+  if (t < n_tiles) iteration(I0{}, t);
+
+  const float l_tot = sum_with_partner32(l_run);
+  if (my_q < Nq) {
+    // This block's partial: O_b = acc / l_tot, LSE_b = m_ref + log2 l_tot
+    // (log2 units).  MERGE folds it into the running (Out, LSE) of the row
+    // with the log-sum-exp identity; LSE = -inf there marks an empty
+    // accumulator whose O is not read.
+    const size_t lrow = (size_t)bh * Nq + my_q;
+    const float lse_b = m_ref + fast_log2(l_tot);
+    float wb = 1.f / l_tot, wa = 0.f, lse_new = lse_b;
+    bool has_a = false;
+    if constexpr (MERGE) {
+      const float la = LSE[lrow] * kLog2e;
+      has_a = la != -INFINITY;
+      if (has_a) {
+        const float m = fmaxf(la, lse_b);
+        const float ea = fast_exp2(la - m), eb = fast_exp2(lse_b - m);
+        const float inv = 1.f / (ea + eb);
+        wa = ea * inv;
+        wb = eb * inv / l_tot;
+        lse_new = m + fast_log2(ea + eb);
+      }
+    }
+    const size_t orow = lrow * D;
+#pragma unroll
+    for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * hi;
+        if (d0 < D) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[dt][4 * g + e] * wb;
+          if constexpr (OUT_F32) {
+            f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
+            if (MERGE && has_a) {
+              const f32x4 a = *p;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], o[e]);
+            }
+            *p = f32x4{o[0], o[1], o[2], o[3]};
+          } else {
+            bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
+            if (MERGE && has_a) {
+              const bf16x4 a = *p;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], o[e]);
+            }
+            *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+          }
+        }
+      }
+    if (hi == 0) LSE[lrow] = lse_new * kLn2;
+  }
+}
+
+}  // namespace
+
+// Launch for one head dim (explicitly instantiated in the attn_bf16_d*.hip
+// files so the instantiations compile in parallel).
+template <int D>
+hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH,
+                         int Nq, int Nkv, float scale, bool out_f32, bool merge,
+                         hipStream_t stream) {
+  const int n_qtiles = (Nq + kBr - 1) / kBr;
+  const dim3 grid((unsigned)(n_qtiles * BH));
+  const float c2 = scale * kLog2e;
+  const __bf16* q = static_cast<const __bf16*>(Q);
+  const __bf16* k = static_cast<const __bf16*>(K);
+  const __bf16* v = static_cast<const __bf16*>(V);
+  if (out_f32) {
+    if (merge)
+      attn_fwd_bf16_kernel<D, true, true><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+    else
+      attn_fwd_bf16_kernel<D, true, false><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+  } else {
+    if (merge)
+      attn_fwd_bf16_kernel<D, false, true><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+    else
+      attn_fwd_bf16_kernel<D, false, false><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dit

@@ -22,7 +22,7 @@ constexpr int kTile = 32;  // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int D>
+template <int D, bool MERGE>
 __global__ __launch_bounds__(kRows) void attn_fwd_f32_kernel(const float* __restrict__ Q,
                                                              const float* __restrict__ K,
                                                              const float* __restrict__ V,
@@ -85,30 +85,55 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32_kernel(const float* __rest
   }
 
   if (row < Nq) {
-    const float inv = 1.f / l_run;
+    // MERGE folds this block's partial into the running (O, LSE) of the row
+    // (log-sum-exp identity; LSE = -inf there marks an empty accumulator).
+    const size_t lrow = (size_t)bh * Nq + row;
+    const float lse_b = m_run + __builtin_amdgcn_logf(l_run);  // log2 units
+    float wb = 1.f / l_run, wa = 0.f, lse_new = lse_b;
+    bool has_a = false;
+    if constexpr (MERGE) {
+      const float la = LSE[lrow] * kLog2e;
+      has_a = la != -INFINITY;
+      if (has_a) {
+        const float m = fmaxf(la, lse_b);
+        const float ea = __builtin_amdgcn_exp2f(la - m), eb = __builtin_amdgcn_exp2f(lse_b - m);
+        wa = ea / (ea + eb);
+        wb = eb / (ea + eb) / l_run;
+        lse_new = m + __builtin_amdgcn_logf(ea + eb);
+      }
+    }
 #pragma unroll
-    for (int t = 0; t < D; ++t) O[((size_t)bh * Nq + row) * D + t] = o[t] * inv;
-    LSE[(size_t)bh * Nq + row] = (m_run + __builtin_amdgcn_logf(l_run)) * kLn2;
+    for (int t = 0; t < D; ++t) {
+      float* p = O + lrow * D + t;
+      float v = o[t] * wb;
+      if (MERGE && has_a) v = fmaf(wa, *p, v);
+      *p = v;
+    }
+    LSE[lrow] = lse_new * kLn2;
   }
 }
 
 template <int D>
 hipError_t launch_d(const float* Q, const float* K, const float* V, float* O, float* LSE, int BH,
-                    int Nq, int Nkv, float scale, hipStream_t stream) {
+                    int Nq, int Nkv, float scale, bool merge, hipStream_t stream) {
   const int n_qtiles = (Nq + kRows - 1) / kRows;
-  attn_fwd_f32_kernel<D><<<dim3((unsigned)(n_qtiles * BH)), kRows, 0, stream>>>(
-      Q, K, V, O, LSE, Nq, Nkv, n_qtiles, scale * kLog2e);
+  const dim3 grid((unsigned)(n_qtiles * BH));
+  if (merge)
+    attn_fwd_f32_kernel<D, true><<<grid, kRows, 0, stream>>>(Q, K, V, O, LSE, Nq, Nkv, n_qtiles, scale * kLog2e);
+  else
+    attn_fwd_f32_kernel<D, false><<<grid, kRows, 0, stream>>>(Q, K, V, O, LSE, Nq, Nkv, n_qtiles, scale * kLog2e);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
-                           int BH, int Nq, int Nkv, int d, float scale, hipStream_t stream) {
+                           int BH, int Nq, int Nkv, int d, float scale, bool merge,
+                           hipStream_t stream) {
   switch (d) {
 #define DIT_CASE(DD) \
   case DD:           \
-    return launch_d<DD>(Q, K, V, O, LSE, BH, Nq, Nkv, scale, stream);
+    return launch_d<DD>(Q, K, V, O, LSE, BH, Nq, Nkv, scale, merge, stream);
     DIT_CASE(8) DIT_CASE(16) DIT_CASE(24) DIT_CASE(32) DIT_CASE(40) DIT_CASE(48) DIT_CASE(56)
     DIT_CASE(64) DIT_CASE(72) DIT_CASE(80) DIT_CASE(88) DIT_CASE(96) DIT_CASE(104) DIT_CASE(112)
     DIT_CASE(120) DIT_CASE(128)

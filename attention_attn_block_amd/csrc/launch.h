@@ -7,14 +7,18 @@
 
 namespace dit {
 
-// Attention with bfloat16 Q/K/V (matrix cores), fp32 or bf16 output.
+// Attention with bfloat16 Q/K/V (matrix cores), fp32 or bf16 output.  With
+// `merge`, (O, LSE) hold a running partial that the block's result is folded
+// into (LSE = -inf: empty) instead of being overwritten.
 hipError_t launch_attn_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                            int BH, int Nq, int Nkv, int d, float scale, bool out_f32,
+                            int BH, int Nq, int Nkv, int d, float scale, bool out_f32, bool merge,
                             hipStream_t stream);
 
-// Attention with float32 Q/K/V/O (vector ALU, no reduced-precision products).
+// Attention with float32 Q/K/V/O (vector ALU, no reduced-precision products);
+// `merge` as for launch_attn_bf16.
 hipError_t launch_attn_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
-                           int BH, int Nq, int Nkv, int d, float scale, hipStream_t stream);
+                           int BH, int Nq, int Nkv, int d, float scale, bool merge,
+                           hipStream_t stream);
 
 // In-place log-sum-exp merge a <- a (+) b over `rows` rows of width d.
 hipError_t launch_lse_merge(void* Oa, float* La, const void* Ob, const float* Lb,
@@ -30,5 +34,12 @@ hipError_t launch_splice2(const void* src0, void* dst0, const void* src1, void* 
 // out = u + s * (c - u) over n floats.
 hipError_t launch_cfg(const float* u, const float* c, float* out, long long n, float s,
                       hipStream_t stream);
+
+// CFG combine plus rel-MAE = sum|c - u| / sum|u|: per-block partial sums go to
+// `work` (cfg_relmae_work_floats(n) floats), a second launch reduces them in
+// a fixed order and writes the ratio to *relmae.
+long long cfg_relmae_work_floats(long long n);
+hipError_t launch_cfg_relmae(const float* u, const float* c, float* out, long long n, float s,
+                             float* work, float* relmae, hipStream_t stream);
 
 }  // namespace dit

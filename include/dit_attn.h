@@ -25,8 +25,9 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every pointer is a device pointer owned by the caller and must be 16-byte
- *    aligned.  The library allocates no memory, keeps no per-call state and
- *    needs no workspace.
+ *    aligned.  The library allocates no memory and keeps no per-call state;
+ *    the one call that needs scratch (cfg_combine_relmae) takes it from the
+ *    caller.
  *  - Work is enqueued on `stream` (0 = the null stream) and returns without
  *    synchronising.  Calls on different streams may run concurrently.
  *  - Tensors are row-major and contiguous: [B, H, N, d] with d innermost;
@@ -88,6 +89,25 @@ dit_status_t attn_block_fwd(const void* Q, const void* K, const void* V,
                             hipStream_t stream);
 
 /*
+ * Fused ring step: block attention of Q against this KV block, folded into a
+ * running partial (O_acc, LSE_acc) in the kernel epilogue.  The result equals
+ * attn_block_fwd into temporaries followed by attn_lse_merge(O_acc, LSE_acc,
+ * O_tmp, LSE_tmp), without writing or re-reading the block partial.  This is
+ * the per-device step of Ring and Torus attention, which fold each KV block
+ * (or chunk) as it arrives (SwiftFusion, sections 1-2).
+ *   Q: [B,H,Nq,d], K, V: [B,H,Nkv,d] in_dtype              (read only)
+ *   O_acc: [B,H,Nq,d] acc_dtype, LSE_acc: [B,H,Nq] float32  (read and written)
+ * A row with LSE_acc = -inf is empty: its O_acc is not read and the block's
+ * result is stored (so the first block needs no separate call: fill LSE_acc
+ * with -inf).  Same argument rules and return codes as attn_block_fwd.
+ */
+dit_status_t attn_block_fwd_merge(const void* Q, const void* K, const void* V,
+                                  void* O_acc, float* LSE_acc,
+                                  int B, int H, int Nq, int Nkv, int d, float scale,
+                                  dit_dtype_t in_dtype, dit_dtype_t acc_dtype,
+                                  hipStream_t stream);
+
+/*
  * Log-sum-exp merge of two partials over disjoint key sets, in place into a.
  *
  * Per row r (rows = B*H*Nq):
@@ -145,6 +165,27 @@ dit_status_t attn_patch_fwd(const void* Q_p, const void* K_p, const void* V_p,
  */
 dit_status_t cfg_combine(const float* eps_u, const float* eps_c, float* out,
                          long long n, float s, hipStream_t stream);
+
+/*
+ * CFG combine fused with the cond/uncond discrepancy signal.  Hybridiff
+ * switches between its sequential and parallel phases on a relative mean
+ * absolute error between the conditional and unconditional noise
+ * ("Accelerating Diffusion via Hybrid Data-Pipeline Parallelism ...",
+ * Technische Zusammenfassung, 2.B); the page gives no formula, and the
+ * reading used here is
+ *   relmae = sum_i |eps_c[i] - eps_u[i]| / sum_i |eps_u[i]|   (0 if both are 0)
+ * out is computed exactly as cfg_combine computes it.  The sums are reduced
+ * per workgroup into `workspace`, then in a fixed order (deterministic).
+ *   eps_u, eps_c, out: [n] float32 (out may be exactly eps_u or eps_c)
+ *   workspace: device float32 array of cfg_combine_relmae_workspace(n) entries,
+ *              owned by the caller, scratch (contents on return unspecified)
+ *   relmae: device pointer to one float32, written
+ * workspace and relmae must not overlap the tensors or each other.
+ */
+long long cfg_combine_relmae_workspace(long long n);
+dit_status_t cfg_combine_relmae(const float* eps_u, const float* eps_c, float* out,
+                                long long n, float s, float* workspace, float* relmae,
+                                hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char* dit_status_string(dit_status_t status);

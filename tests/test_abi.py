@@ -37,7 +37,7 @@ def lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(\w+)\s*\(", src, flags=re.M)))
 
 
 def test_header_declares_the_calls():
@@ -164,6 +164,59 @@ def cfg(lib, **kw):
 ])
 def test_cfg_combine_rejects(lib, kw, code):
     assert cfg(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# attn_block_fwd_merge
+# ---------------------------------------------------------------------------
+
+def fused(lib, **kw):
+    a = dict(Q=ptr(0), K=ptr(1), V=ptr(2), O=ptr(3), LSE=ptr(4), B=1, H=2, Nq=100, Nkv=70, d=128,
+             scale=0.088, i=BF16, o=F32)
+    a.update(kw)
+    return lib.attn_block_fwd_merge(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"],
+                                    a["Nq"], a["Nkv"], a["d"], a["scale"], a["i"], a["o"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), INV), (dict(O=None), INV), (dict(LSE=None), INV), (dict(Nkv=0), INV),
+    (dict(scale=-0.5), INV), (dict(o=9), INV), (dict(O=ptr(3, 8)), INV),
+    (dict(d=130), UNS), (dict(i=F32, o=BF16), UNS),
+    (dict(O=ptr(2, 32)), INV),                   # accumulator overlaps V
+    (dict(LSE=ptr(3, 1024)), INV),               # LSE_acc inside O_acc
+])
+def test_attn_block_fwd_merge_rejects(lib, kw, code):
+    assert fused(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
+# cfg_combine_relmae
+# ---------------------------------------------------------------------------
+
+def relmae(lib, **kw):
+    a = dict(u=ptr(0), c=ptr(1), o=ptr(2), n=8192, s=4.0, w=ptr(3), r=ptr(4))
+    a.update(kw)
+    return lib.cfg_combine_relmae(a["u"], a["c"], a["o"], a["n"], a["s"], a["w"], a["r"], None)
+
+
+def test_relmae_workspace_size(lib):
+    assert lib.cfg_combine_relmae_workspace(0) == 0
+    assert lib.cfg_combine_relmae_workspace(1) == 2
+    assert lib.cfg_combine_relmae_workspace(4096) == 2
+    assert lib.cfg_combine_relmae_workspace(8192) == 4
+    assert lib.cfg_combine_relmae_workspace(4 * 1024 + 4) == 4
+    assert lib.cfg_combine_relmae_workspace(1 << 26) == 2 * (1 << 14)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), INV), (dict(w=None), INV), (dict(r=None), INV), (dict(n=0), INV),
+    (dict(s=math.inf), INV), (dict(w=ptr(3, 4)), INV), (dict(r=ptr(4, 8)), INV),
+    (dict(o=ptr(1, 16)), INV),                   # out partially overlaps eps_c
+    (dict(w=ptr(2, 64)), INV),                   # workspace inside out
+    (dict(r=ptr(3)), INV),                       # result aliases the workspace
+])
+def test_cfg_combine_relmae_rejects(lib, kw, code):
+    assert relmae(lib, **kw) == code
 
 
 # ---------------------------------------------------------------------------

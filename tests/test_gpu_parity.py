@@ -10,8 +10,8 @@ import pytest
 import torch
 
 import oracle
-from attention_attn_block_amd import (attn_block_fwd, attn_lse_merge, attn_patch_fwd,
-                                      cfg_combine, inputs)
+from attention_attn_block_amd import (attn_block_fwd, attn_block_fwd_merge, attn_lse_merge,
+                                      attn_patch_fwd, cfg_combine, cfg_combine_relmae, inputs)
 from tests.gpu_util import (assert_bf16_close, assert_close, assert_f32_close, to_f64,
                             to_oracle)
 
@@ -283,3 +283,81 @@ def test_deterministic_and_stream_ordered():
         O2 = O2.clone()
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+# ---------------------------------------------------------------------------
+# Fused ring step and the CFG discrepancy signal
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("acc_dtype", [torch.float32, torch.bfloat16])
+def test_ring_2048px_fused_merge(acc_dtype):
+    """attn_block_fwd_merge over the 8 KV blocks, starting from an empty
+    accumulator (LSE = -inf, O full of NaN that must never be read), equals
+    attention over all 16384 keys."""
+    w = inputs.ring_2048px()
+    q = dev(w["q"])
+    B, H, Nq, d = q.shape
+    o_acc = torch.full((B, H, Nq, d), float("nan"), dtype=acc_dtype, device="cuda:0")
+    l_acc = torch.full((B, H, Nq), -float("inf"), device="cuda:0")
+    say("case ring fused", acc_dtype)
+    for kj, vj in zip(w["ks"], w["vs"]):
+        attn_block_fwd_merge(q, dev(kj), dev(vj), o_acc, l_acc, scale=w["scale"])
+    torch.cuda.synchronize()
+    K = torch.cat(w["ks"], dim=2)
+    V = torch.cat(w["vs"], dim=2)
+    Or, Lr = oracle.ref_attn(to_oracle(w["q"]), to_oracle(K), to_oracle(V), w["scale"])
+    assert_bf16_close(to_f64(o_acc), Or, "ring fused O")
+    assert_bf16_close(to_f64(l_acc), Lr, "ring fused LSE")
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 70, 45, 72), (2, 1, 130, 257, 128), (1, 1, 1, 3, 8)])
+def test_fused_merge_uneven_blocks(shape):
+    """Three KV blocks of unequal length, fused, against the oracle's fold of
+    the same blocks and its full attention; the fp32 path too."""
+    B, H, Nq, Nkv, d = shape
+    for dt in ("bf16", "f32"):
+        q, k, v = inputs.attn_inputs(B, H, Nq, Nkv, d, dt, seed=Nq + Nkv)
+        cuts = [0, Nkv // 3, (2 * Nkv) // 3 + 1, Nkv]
+        cuts = sorted(set(min(max(c, 0), Nkv) for c in cuts))
+        acc_t = torch.float32
+        o_acc = torch.zeros((B, H, Nq, d), dtype=acc_t, device="cuda:0")
+        l_acc = torch.full((B, H, Nq), -float("inf"), device="cuda:0")
+        say("case fused uneven", shape, dt, cuts)
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            attn_block_fwd_merge(dev(q), dev(k[:, :, a:b].contiguous()), dev(v[:, :, a:b].contiguous()),
+                                 o_acc, l_acc, scale=inputs.default_scale(d))
+        torch.cuda.synchronize()
+        Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), inputs.default_scale(d))
+        assert_close(to_f64(o_acc), Or, dt == "f32", "fused O")
+        assert_close(to_f64(l_acc), Lr, dt == "f32", "fused LSE")
+
+
+@pytest.mark.parametrize("n", [1, 5, 4096, 8192, 4096 * 3 + 7, (1 << 22) + 1])
+def test_cfg_relmae(n):
+    g = torch.Generator().manual_seed(1000 + n)
+    u = torch.randn(n, generator=g)
+    c = u + 0.3 * torch.randn(n, generator=g)
+    say("case cfg relmae n =", n)
+    out, rm = cfg_combine_relmae(dev(u), dev(c), 4.0)
+    torch.cuda.synchronize()
+    assert_f32_close(to_f64(out), oracle.ref_cfg(to_oracle(u), to_oracle(c), 4.0), "relmae cfg out")
+    want = oracle.ref_cfg_relmae(to_oracle(u), to_oracle(c))
+    got = float(rm.item())
+    assert abs(got - want) <= 1e-5 * abs(want), (got, want)
+    # deterministic: a second call gives the same bits
+    out2, rm2 = cfg_combine_relmae(dev(u), dev(c), 4.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(rm, rm2)
+
+
+def test_cfg_relmae_dit_xl_256_and_identity():
+    w = inputs.dit_xl_256()
+    say("case relmae dit_xl_256")
+    out, rm = cfg_combine_relmae(dev(w["eps_u"]), dev(w["eps_c"]), w["s"])
+    same, rz = cfg_combine_relmae(dev(w["eps_u"]), dev(w["eps_u"]), w["s"])
+    zeros, r00 = cfg_combine_relmae(torch.zeros(64, device="cuda:0"), torch.zeros(64, device="cuda:0"), 2.0)
+    torch.cuda.synchronize()
+    want = oracle.ref_cfg_relmae(to_oracle(w["eps_u"]), to_oracle(w["eps_c"]))
+    assert abs(float(rm.item()) - want) <= 1e-5 * want
+    assert float(rz.item()) == 0.0 and float(r00.item()) == 0.0
+    assert_f32_close(to_f64(out), oracle.ref_cfg(to_oracle(w["eps_u"]), to_oracle(w["eps_c"]), w["s"]), "cfg")
