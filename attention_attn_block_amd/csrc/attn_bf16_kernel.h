@@ -132,11 +132,16 @@ __device__ __forceinline__ int swz_v(int row) {
   else return 0;
 }
 
-// Rescale threshold (log2 units): the running maximum used for the
-// exponentials is only moved when a row's score maximum exceeds it by more
-// than this, so most tiles skip rescaling the output accumulator.  Weights
-// stay below 2^8 and the result is unchanged in exact arithmetic.
+// Lazy rescaling.  The reference max m_ref used for the exponentials is not
+// tracked per tile.  A lane's 32 weights of a tile are accepted while their
+// sum (needed for the normaliser anyway) is at most kLaneSumLimit, which
+// bounds every weight by 2^14 -- harmless in bf16 and in the fp32
+// accumulators.  A larger sum (or inf) sends the wave down the rare path: the
+// rows whose maximum exceeds the reference by more than kTau (log2 units) move
+// the reference to that maximum and rescale what they accumulated.  The
+// result is unchanged in exact arithmetic.
 constexpr float kTau = 8.f;
+constexpr float kLaneSumLimit = 32.f * 512.f;
 
 template <int D, bool OUT_F32, bool MERGE>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const bool full = kv0 + kBc <= Nkv;
 #pragma unroll
     for (int j = 0; j < G::kKLoads; ++j) {
-      const int first_unit = 64 * (4 * j + wv);
+      const int first_unit = 64 * ((kThreads / 64) * j + wv);
       if (first_unit < kTileUnits) {  // wave-uniform: kTileUnits is a multiple of 64
         int off = goff[j];
         if (!full) {  // ragged last tile: clamp rows into the block
@@ -298,7 +303,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
     m_ref = max_with_partner32(mx) * c2;
   }
+  {
+    const float neg_m = -m_ref;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_cur[kt][r] = fmaf(s_cur[kt][r], c2, neg_m);
+  }
 
+  // s_cur holds tile t's scores already in the exponent form
+  // t = s * scale * log2(e) - m_ref.
   auto iteration = [&](auto buf_c, int t) {
     constexpr int cur = decltype(buf_c)::value;  // = t % 2
     constexpr int nxt = cur ^ 1;
@@ -312,20 +326,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     f32x16 s_nxt[2];
     qk(nxt, s_nxt);
 
-    const float neg_m = -m_ref;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_cur[kt][r] = fmaf(s_cur[kt][r], c2, neg_m);
-    float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
     bf16x8 pb[4];
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
       for (int j = 0; j < 8; ++j) pb[ch][j] = (__bf16)fast_exp2(s_cur[ch >> 1][8 * (ch & 1) + j]);
-    mx = max_with_partner32(mx);
+    // The normaliser sums the same bf16 weights the product uses; this lane's
+    // share of it also bounds every weight the lane holds.
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][0], pb[ch][1]}, ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][2], pb[ch][3]}, ones, ls1, false);
+      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][4], pb[ch][5]}, ones, ls0, false);
+      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][6], pb[ch][7]}, ones, ls1, false);
+    }
+    float ls = ls0 + ls1;
     // Issue order for this block: K-operand LDS reads two products ahead,
     // then per product one MFMA, the next read and a share of the softmax
     // VALU work, so the vector ALU runs while the matrix core is busy.
@@ -334,12 +350,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int i = 0; i < 2 * G::kChunks; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 96 / G::kChunks, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 64 / G::kChunks, 0);  // VALU
     }
-    const bool grow = mx > kTau;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      // Rare: move the reference to this tile's max for the rows that grew
-      // past it, rescale what was accumulated, recompute this tile's weights.
+
+    // Rare: a lane's share of the sum exceeds the limit (so some weight there
+    // exceeds 2^9), i.e. a row's scores grew well past the reference max.
+    // Move the reference to the tile's max for the rows that grew past kTau,
+    // rescale what was accumulated and recompute this tile's weights.
+    if (__builtin_amdgcn_ballot_w64(!(ls <= kLaneSumLimit))) {
+      float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
+      mx = max_with_partner32(mx);
+      const bool grow = mx > kTau;
       const float delta = grow ? mx : 0.f;
       const float alpha = fast_exp2(-delta);
       l_run *= alpha;
@@ -348,22 +371,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
       m_ref += delta;
+      ls0 = 0.f;
+      ls1 = 0.f;
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch)
+      for (int ch = 0; ch < 4; ++ch) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const __bf16 re = (__bf16)fast_exp2(s_cur[ch >> 1][8 * (ch & 1) + j] - delta);
           pb[ch][j] = grow ? re : pb[ch][j];
         }
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][0], pb[ch][1]}, ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][2], pb[ch][3]}, ones, ls1, false);
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][4], pb[ch][5]}, ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][6], pb[ch][7]}, ones, ls1, false);
+      }
+      ls = ls0 + ls1;
     }
+    l_run += ls;
 
-    // ---- O^T += V^T P^T (16 keys per product) and the row sums ----
-    // Slot j of half-wave h holds key 8 (j / 4) + 4 h + j % 4 of the chunk on
-    // both operands.
+    // ---- O^T += V^T P^T (16 keys per product); vector ALU: exponent form of
+    // tile t + 1's scores.  Slot j of half-wave h holds key 8 (j / 4) + 4 h +
+    // j % 4 of the chunk on both operands.
     const __bf16* vb = reinterpret_cast<const __bf16*>(v_lds[cur]);
-    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+    for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
       for (int dt = 0; dt < G::kDTiles; ++dt) {
         const __bf16* vp = vb + v_off[dt] + 16 * ch * G::kOct * 8;
@@ -372,12 +403,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
         acc[dt] = mfma32(a, pb[ch], acc[dt]);
       }
-      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][0], pb[ch][1]}, ones, ls0, false);
-      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][2], pb[ch][3]}, ones, ls1, false);
-      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][4], pb[ch][5]}, ones, ls0, false);
-      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][6], pb[ch][7]}, ones, ls1, false);
-    }
-    l_run += ls0 + ls1;
+    const float neg_m = -m_ref;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_nxt[kt][r] = fmaf(s_nxt[kt][r], c2, neg_m);
 
     dma_wait();
     __syncthreads();

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void splice2_kernel(const u32x4* __restri
   u32x4* t = dst + seg * dst_seg_stride + dst_offset;
   const long long stride = (long long)gridDim.x * kThreads;
   for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < seg_units; i += stride)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), t + i);
+    t[i] = s[i];  // plain accesses: the fresh patch is usually cache-resident
 }
 
 // ---------------------------------------------------------------------------

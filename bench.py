@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "attn_fwd_bf16_d128_video_patch_traffic.txt")
-ATTN_SRC = os.path.join(ROOT, "attention_attn_block_amd", "csrc", "attn_bf16.hip")
+ATTN_SRC = os.path.join(ROOT, "attention_attn_block_amd", "csrc", "attn_bf16_kernel.h")
 
 
 def parse():
@@ -223,7 +223,7 @@ def main():
     # ---- supplementary, outside the timed region ---------------------------------
     supp = {}
     if not args.no_supplementary:
-        supp = supplementary(torch, dev, attn_block_fwd, attn_lse_merge, cfg_combine, inputs)
+        supp = supplementary(torch, dev, inputs, q_r, ks, vs, wr["scale"])
 
     roofline = {"bound": "mfma", "achieved": patch_tflops, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": patch_tflops / PEAK_BF16_TFLOPS,
@@ -252,9 +252,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def supplementary(torch, dev, attn_block_fwd, attn_lse_merge, cfg_combine, inputs):
+def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):
     """Reported beside the step: merge and CFG on cold HBM (rotating buffers
-    larger than the 256 MB Infinity Cache), and the d=72 workloads."""
+    larger than the 256 MB Infinity Cache), the fused ring step, and the d=72
+    workloads."""
+    from attention_attn_block_amd import (attn_block_fwd, attn_block_fwd_merge, attn_lse_merge,
+                                          cfg_combine, cfg_combine_relmae)
     res = {}
 
     def timed(fn, iters):
@@ -281,16 +284,35 @@ def supplementary(torch, dev, attn_block_fwd, attn_lse_merge, cfg_combine, input
                                       "bytes": nbytes}
     del sets
 
-    # CFG combine at 2^26 floats per tensor (768 MB per call).
+    # CFG combine (and with the rel-MAE signal) at 2^26 floats per tensor (768 MB per call).
     n = 1 << 26
     u, c, o = (torch.randn(n, device=dev) for _ in range(3))
-    fn = lambda i: cfg_combine(u, c, 4.0, out=o)
-    fn(0)
-    us = timed(fn, 20)
-    nbytes = 3 * n * 4
-    res["cfg_combine_2^26"] = {"us": us, "gbs": nbytes / us / 1e3,
-                               "frac_hbm_peak": nbytes / us / 1e3 / PEAK_HBM_GBS}
+    ws = torch.empty(1 << 16, device=dev)
+    rm = torch.empty(4, device=dev)[:1]
+    for name, fn in (("cfg_combine_2^26", lambda i: cfg_combine(u, c, 4.0, out=o)),
+                     ("cfg_combine_relmae_2^26",
+                      lambda i: cfg_combine_relmae(u, c, 4.0, out=o, workspace=ws, relmae=rm))):
+        fn(0)
+        us = timed(fn, 20)
+        nbytes = 3 * n * 4
+        res[name] = {"us": us, "gbs": nbytes / us / 1e3, "frac_hbm_peak": nbytes / us / 1e3 / PEAK_HBM_GBS}
     del u, c, o
+
+    # Ring share with the merge fused into the attention epilogue.
+    B, H, Nq, dd = q_r.shape
+    o_acc = torch.empty((B, H, Nq, dd), dtype=torch.float32, device=dev)
+    l_acc = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+
+    def ring_fused(i):
+        l_acc.fill_(-float("inf"))
+        for kj, vj in zip(ks, vs):
+            attn_block_fwd_merge(q_r, kj, vj, o_acc, l_acc, scale=ring_scale)
+
+    ring_fused(0)
+    us = timed(ring_fused, 20)
+    f = len(ks) * attn_flops(B, H, Nq, ks[0].shape[2], dd)
+    res["ring_share_fused_merge"] = {"us_per_share": us, "tflops": f / (us * 1e-6) / 1e12,
+                                     "frac_bf16_peak": f / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
 
     # d = 72 attention: PixArt-style 1024 px and DiT-XL/2 256 px.
     for name in ("pixart_1024", "dit_xl_256"):
