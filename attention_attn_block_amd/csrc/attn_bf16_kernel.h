@@ -60,7 +60,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kBr = 128;        // query rows per workgroup
-constexpr int kBc = 64;         // keys per KV tile
+constexpr int kBc = 64;         // keys per KV tile (a multiple of 32)
+constexpr int kKT = kBc / 32;   // 32-key score accumulators per tile
+constexpr int kCH = kBc / 16;   // 16-key chunks of the PV product per tile
+constexpr int kWavesPerSimd = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -141,10 +144,20 @@ __device__ __forceinline__ int swz_v(int row) {
 // the reference to that maximum and rescale what they accumulated.  The
 // result is unchanged in exact arithmetic.
 constexpr float kTau = 8.f;
-constexpr float kLaneSumLimit = 32.f * 512.f;
+constexpr float kLaneSumLimit = 16.f * kKT * 512.f;
+
+// Max over this lane's kKT x 16 scores of a tile.
+__device__ __forceinline__ float row_max(const f32x16* s) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  return mx;
+}
 
 template <int D, bool OUT_F32, bool MERGE>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     void* __restrict__ Out, float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, float c2) {
   using G = Geo<D>;
@@ -210,7 +223,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < G::kKLoads; ++j) {
       const int first_unit = 64 * ((kThreads / 64) * j + wv);
-      if (first_unit < kTileUnits) {  // wave-uniform: kTileUnits is a multiple of 64
+      // Wave-uniform skip of loads past the tile; when the tile is not a whole
+      // number of 64-unit wave loads, the lanes past its end must not load.
+      const bool lane_in = (kTileUnits % 64 == 0) || tid + kThreads * j < kTileUnits;
+      if (first_unit < kTileUnits && lane_in) {
         int off = goff[j];
         if (!full) {  // ragged last tile: clamp rows into the block
           const int over = kv0 + g_row[j] - (Nkv - 1);
@@ -234,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   // S^T = K Q^T for the 64 keys of the K tile in LDS buffer `buf`.
   auto qk = [&](int buf, f32x16* s) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < kKT; ++kt) {
       s[kt] = f32x16{};
 #pragma unroll
       for (int c = 0; c < G::kChunks; ++c) {
@@ -252,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   auto mask_tail = [&](f32x16* s, int kv0) {
     if (kv0 + kBc > Nkv) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -292,21 +308,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   dma_wait();
   __syncthreads();
 
-  f32x16 s_cur[2];
+  f32x16 s_cur[kKT];
   qk(0, s_cur);
   mask_tail(s_cur, 0);
   // Reference max from tile 0 (later tiles only move it by more than kTau).
   float m_ref;
   {
-    float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
+    const float mx = row_max(s_cur);
     m_ref = max_with_partner32(mx) * c2;
   }
   {
     const float neg_m = -m_ref;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_cur[kt][r] = fmaf(s_cur[kt][r], c2, neg_m);
   }
@@ -323,19 +337,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     // ---- matrix cores: S for tile t + 1; vector ALU: weights of tile t ----
     // (Branch-free so the two interleave.  On the last tile the product reads
     // an allocated, unused K buffer and its result is dropped.)
-    f32x16 s_nxt[2];
+    f32x16 s_nxt[kKT];
     qk(nxt, s_nxt);
 
-    bf16x8 pb[4];
+    bf16x8 pb[kCH];
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch)
+    for (int ch = 0; ch < kCH; ++ch)
 #pragma unroll
       for (int j = 0; j < 8; ++j) pb[ch][j] = (__bf16)fast_exp2(s_cur[ch >> 1][8 * (ch & 1) + j]);
     // The normaliser sums the same bf16 weights the product uses; this lane's
     // share of it also bounds every weight the lane holds.
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
+    for (int ch = 0; ch < kCH; ++ch) {
       ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][0], pb[ch][1]}, ones, ls0, false);
       ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][2], pb[ch][3]}, ones, ls1, false);
       ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][4], pb[ch][5]}, ones, ls0, false);
@@ -347,10 +361,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     // VALU work, so the vector ALU runs while the matrix core is busy.
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // LDS read
 #pragma unroll
-    for (int i = 0; i < 2 * G::kChunks; ++i) {
+    for (int i = 0; i < kKT * G::kChunks; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 64 / G::kChunks, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 32 * kKT / G::kChunks, 0);  // VALU
     }
 
     // Rare: a lane's share of the sum exceeds the limit (so some weight there
@@ -358,10 +372,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     // Move the reference to the tile's max for the rows that grew past kTau,
     // rescale what was accumulated and recompute this tile's weights.
     if (__builtin_amdgcn_ballot_w64(!(ls <= kLaneSumLimit))) {
-      float mx = fmaxf(s_cur[0][0], s_cur[1][0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
-      mx = max_with_partner32(mx);
+      const float mx = max_with_partner32(row_max(s_cur));
       const bool grow = mx > kTau;
       const float delta = grow ? mx : 0.f;
       const float alpha = fast_exp2(-delta);
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       ls0 = 0.f;
       ls1 = 0.f;
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
+      for (int ch = 0; ch < kCH; ++ch) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const __bf16 re = (__bf16)fast_exp2(s_cur[ch >> 1][8 * (ch & 1) + j] - delta);
@@ -394,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     // j % 4 of the chunk on both operands.
     const __bf16* vb = reinterpret_cast<const __bf16*>(v_lds[cur]);
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch)
+    for (int ch = 0; ch < kCH; ++ch)
 #pragma unroll
       for (int dt = 0; dt < G::kDTiles; ++dt) {
         const __bf16* vp = vb + v_off[dt] + 16 * ch * G::kOct * 8;
@@ -405,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       }
     const float neg_m = -m_ref;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s_nxt[kt][r] = fmaf(s_nxt[kt][r], c2, neg_m);
 
@@ -413,8 +424,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     __syncthreads();
     if (has1) {
       mask_tail(s_nxt, (t + 1) * kBc);
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) s_cur[kt] = s_nxt[kt];
     }
   };
 
