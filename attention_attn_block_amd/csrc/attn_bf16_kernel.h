@@ -59,11 +59,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;   // 4 waves
-constexpr int kBr = 128;        // query rows per workgroup
 constexpr int kBc = 64;         // keys per KV tile (a multiple of 32)
 constexpr int kKT = kBc / 32;   // 32-key score accumulators per tile
 constexpr int kCH = kBc / 16;   // 16-key chunks of the PV product per tile
-constexpr int kWavesPerSimd = 2;
+constexpr int kWavesPerSimd = 2;  // with one query group per wave
+constexpr int kGroups = 1;        // query groups of 32 rows per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -156,12 +156,18 @@ __device__ __forceinline__ float row_max(const f32x16* s) {
   return mx;
 }
 
-template <int D, bool OUT_F32, bool MERGE>
-__global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
+// NG = query groups of 32 rows per wave.  NG = 2 lets every K and V operand
+// read from LDS (and every tile loaded into LDS) feed twice the matrix work,
+// but its registers (with 32-key tiles; 64-key tiles spill) allow only one
+// wave per SIMD, and on MI355X that ran about a third slower than NG = 1 with
+// two waves per SIMD, so kGroups is 1.
+template <int D, int NG, bool OUT_F32, bool MERGE>
+__global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     void* __restrict__ Out, float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, float c2) {
   using G = Geo<D>;
-  // K and V tiles: 64 rows of kOct 16-byte units each, unit-swizzled (see
+  constexpr int kRowsWG = (kThreads / 64) * 32 * NG;  // query rows per workgroup
+  // K and V tiles: kBc rows of kOct 16-byte units each, unit-swizzled (see
   // swz_k / swz_v), plus slack for the transposing reads of the last rows.
   constexpr int kTileUnits = kBc * G::kOct;
   constexpr int kBufUnits = kTileUnits + 16;
@@ -189,17 +195,21 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
   const __bf16* Kh = K + (size_t)bh * Nkv * D;
   const __bf16* Vh = V + (size_t)bh * Nkv * D;
 
-  const int my_q = qt * kBr + wave * 32 + l32;
-  const int q_ld = my_q < Nq ? my_q : Nq - 1;
-
-  // Q^T as the B operand: lane holds Q[my_q][16c + 8hi .. +7].
-  bf16x8 qf[G::kChunks];
+  // Query rows of this lane, one per group; Q^T as the B operand: lane holds
+  // Q[row][16c + 8hi .. +7].
+  int my_q[NG];
+  bf16x8 qf[NG][G::kChunks];
 #pragma unroll
-  for (int c = 0; c < G::kChunks; ++c) {
-    if (G::kHalfTail && c == G::kChunks - 1 && hi) {
-      qf[c] = bf16x8{};
-    } else {
-      qf[c] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)q_ld * D + 16 * c + 8 * hi);
+  for (int g = 0; g < NG; ++g) {
+    my_q[g] = qt * kRowsWG + (wave * NG + g) * 32 + l32;
+    const int q_ld = my_q[g] < Nq ? my_q[g] : Nq - 1;
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) {
+      if (G::kHalfTail && c == G::kChunks - 1 && hi) {
+        qf[g][c] = bf16x8{};
+      } else {
+        qf[g][c] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)q_ld * D + 16 * c + 8 * hi);
+      }
     }
   }
 
@@ -247,11 +257,13 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
 #pragma unroll
   for (int c = 0; c < G::kChunks; ++c) k_unit[c] = l32 * G::kOct + (((2 * c + hi) ^ sk) % G::kOct);
 
-  // S^T = K Q^T for the 64 keys of the K tile in LDS buffer `buf`.
-  auto qk = [&](int buf, f32x16* s) {
+  // S^T = K Q^T for the kBc keys of the K tile in LDS buffer `buf`; each K
+  // operand read feeds the products of all NG query groups.
+  auto qk = [&](int buf, f32x16 (*s)[kKT]) {
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt) {
-      s[kt] = f32x16{};
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s[g][kt] = f32x16{};
 #pragma unroll
       for (int c = 0; c < G::kChunks; ++c) {
         bf16x8 a;
@@ -260,41 +272,47 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
         } else {
           a = __builtin_bit_cast(bf16x8, k_lds[buf][kt * 32 * G::kOct + k_unit[c]]);
         }
-        s[kt] = mfma32(a, qf[c], s[kt]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) s[g][kt] = mfma32(a, qf[g][c], s[g][kt]);
       }
     }
   };
   // Keys past the end of the block (last tile only) get zero weight.
-  auto mask_tail = [&](f32x16* s, int kv0) {
+  auto mask_tail = [&](f32x16 (*s)[kKT], int kv0) {
     if (kv0 + kBc > Nkv) {
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= Nkv) s[kt][r] = -INFINITY;
-        }
+        for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key >= Nkv) s[g][kt][r] = -INFINITY;
+          }
     }
   };
 
-  // Transposing V reads (see lds_read_tr16): in lane group g = lane / 16,
-  // lane i names row 4 (g / 2) + i / 4 of each 8-key half chunk and columns
-  // 16 (g % 2) + 4 (i % 4) .. +3 of each 32-column d tile.  The row's swizzle
+  // Transposing V reads (see lds_read_tr16): in lane group q = lane / 16,
+  // lane i names row 4 (q / 2) + i / 4 of each 8-key half chunk and columns
+  // 16 (q % 2) + 4 (i % 4) .. +3 of each 32-column d tile.  The row's swizzle
   // depends on i / 4 only, so each d tile gets one lane-constant offset.
-  const int vg = lane >> 4, vi = lane & 15;
-  const int v_row = 4 * (vg >> 1) + (vi >> 2);
+  const int vq = lane >> 4, vi = lane & 15;
+  const int v_row = 4 * (vq >> 1) + (vi >> 2);
   const int sv = swz_v<G::kOct>(v_row);
   int v_off[G::kDTiles];  // bf16 element offsets inside a V buffer
 #pragma unroll
   for (int dt = 0; dt < G::kDTiles; ++dt) {
-    const int unit = 4 * dt + 2 * (vg & 1) + ((vi & 3) >> 1);
+    const int unit = 4 * dt + 2 * (vq & 1) + ((vi & 3) >> 1);
     v_off[dt] = (v_row * G::kOct + (unit ^ sv)) * 8 + 4 * (vi & 1);
   }
 
-  f32x16 acc[G::kDTiles];
+  f32x16 acc[NG][G::kDTiles];
 #pragma unroll
-  for (int t = 0; t < G::kDTiles; ++t) acc[t] = f32x16{};
-  float l_run = 0.f;   // this lane's share of the running normaliser (bf16 weights)
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int t = 0; t < G::kDTiles; ++t) acc[g][t] = f32x16{};
+  float l_run[NG];   // this lane's share of each row's normaliser (bf16 weights)
+  float m_ref[NG];   // reference row max for the exponentials, log2 units
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   const int n_tiles = (Nkv + kBc - 1) / kBc;
 
@@ -308,25 +326,22 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
   dma_wait();
   __syncthreads();
 
-  f32x16 s_cur[kKT];
+  f32x16 s_cur[NG][kKT];
   qk(0, s_cur);
   mask_tail(s_cur, 0);
-  // Reference max from tile 0 (later tiles only move it by more than kTau).
-  float m_ref;
-  {
-    const float mx = row_max(s_cur);
-    m_ref = max_with_partner32(mx) * c2;
-  }
-  {
-    const float neg_m = -m_ref;
+  // Reference max from tile 0; s_cur then holds the exponent form
+  // t = s * scale * log2(e) - m_ref.
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    l_run[g] = 0.f;
+    m_ref[g] = max_with_partner32(row_max(s_cur[g])) * c2;
+    const float neg_m = -m_ref[g];
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_cur[kt][r] = fmaf(s_cur[kt][r], c2, neg_m);
+      for (int r = 0; r < 16; ++r) s_cur[g][kt][r] = fmaf(s_cur[g][kt][r], c2, neg_m);
   }
 
-  // s_cur holds tile t's scores already in the exponent form
-  // t = s * scale * log2(e) - m_ref.
   auto iteration = [&](auto buf_c, int t) {
     constexpr int cur = decltype(buf_c)::value;  // = t % 2
     constexpr int nxt = cur ^ 1;
@@ -337,72 +352,85 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
     // ---- matrix cores: S for tile t + 1; vector ALU: weights of tile t ----
     // (Branch-free so the two interleave.  On the last tile the product reads
     // an allocated, unused K buffer and its result is dropped.)
-    f32x16 s_nxt[kKT];
+    f32x16 s_nxt[NG][kKT];
     qk(nxt, s_nxt);
 
-    bf16x8 pb[kCH];
+    bf16x8 pb[NG][kCH];
+    float ls[NG];
 #pragma unroll
-    for (int ch = 0; ch < kCH; ++ch)
+    for (int g = 0; g < NG; ++g) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[ch][j] = (__bf16)fast_exp2(s_cur[ch >> 1][8 * (ch & 1) + j]);
-    // The normaliser sums the same bf16 weights the product uses; this lane's
-    // share of it also bounds every weight the lane holds.
-    float ls0 = 0.f, ls1 = 0.f;
+      for (int ch = 0; ch < kCH; ++ch)
 #pragma unroll
-    for (int ch = 0; ch < kCH; ++ch) {
-      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][0], pb[ch][1]}, ones, ls0, false);
-      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][2], pb[ch][3]}, ones, ls1, false);
-      ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][4], pb[ch][5]}, ones, ls0, false);
-      ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][6], pb[ch][7]}, ones, ls1, false);
+        for (int j = 0; j < 8; ++j)
+          pb[g][ch][j] = (__bf16)fast_exp2(s_cur[g][ch >> 1][8 * (ch & 1) + j]);
+      // The normaliser sums the same bf16 weights the product uses; this
+      // lane's share of it also bounds every weight the lane holds.
+      float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+      for (int ch = 0; ch < kCH; ++ch) {
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][0], pb[g][ch][1]}, ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][2], pb[g][ch][3]}, ones, ls1, false);
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][4], pb[g][ch][5]}, ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][6], pb[g][ch][7]}, ones, ls1, false);
+      }
+      ls[g] = ls0 + ls1;
     }
-    float ls = ls0 + ls1;
-    // Issue order for this block: K-operand LDS reads two products ahead,
-    // then per product one MFMA, the next read and a share of the softmax
-    // VALU work, so the vector ALU runs while the matrix core is busy.
+    // Issue order for this block: K-operand LDS reads two reads ahead, then
+    // per read the NG products it feeds and a share of the softmax VALU work,
+    // so the vector ALU runs while the matrix core is busy.
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // LDS read
 #pragma unroll
     for (int i = 0; i < kKT * G::kChunks; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 32 * kKT / G::kChunks, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 32 * kKT * NG / G::kChunks, 0);  // VALU
     }
 
-    // Rare: a lane's share of the sum exceeds the limit (so some weight there
-    // exceeds 2^9), i.e. a row's scores grew well past the reference max.
-    // Move the reference to the tile's max for the rows that grew past kTau,
-    // rescale what was accumulated and recompute this tile's weights.
-    if (__builtin_amdgcn_ballot_w64(!(ls <= kLaneSumLimit))) {
-      const float mx = max_with_partner32(row_max(s_cur));
-      const bool grow = mx > kTau;
-      const float delta = grow ? mx : 0.f;
-      const float alpha = fast_exp2(-delta);
-      l_run *= alpha;
+    // Rare: a lane's share of a row's sum exceeds the limit (so some weight
+    // there exceeds 2^9), i.e. the row's scores grew well past its reference
+    // max.  Rows whose tile max exceeds the reference by more than kTau move
+    // the reference to it, rescale what they accumulated and recompute this
+    // tile's weights.
+    bool any_big = false;
 #pragma unroll
-      for (int dt = 0; dt < G::kDTiles; ++dt)
+    for (int g = 0; g < NG; ++g) any_big |= !(ls[g] <= kLaneSumLimit);
+    if (__builtin_amdgcn_ballot_w64(any_big)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      m_ref += delta;
-      ls0 = 0.f;
-      ls1 = 0.f;
+      for (int g = 0; g < NG; ++g) {
+        const float mx = max_with_partner32(row_max(s_cur[g]));
+        const bool grow = mx > kTau;
+        const float delta = grow ? mx : 0.f;
+        const float alpha = fast_exp2(-delta);
+        l_run[g] *= alpha;
 #pragma unroll
-      for (int ch = 0; ch < kCH; ++ch) {
+        for (int dt = 0; dt < G::kDTiles; ++dt)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const __bf16 re = (__bf16)fast_exp2(s_cur[ch >> 1][8 * (ch & 1) + j] - delta);
-          pb[ch][j] = grow ? re : pb[ch][j];
+          for (int r = 0; r < 16; ++r) acc[g][dt][r] *= alpha;
+        m_ref[g] += delta;
+        float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < kCH; ++ch) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const __bf16 re = (__bf16)fast_exp2(s_cur[g][ch >> 1][8 * (ch & 1) + j] - delta);
+            pb[g][ch][j] = grow ? re : pb[g][ch][j];
+          }
+          ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][0], pb[g][ch][1]}, ones, ls0, false);
+          ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][2], pb[g][ch][3]}, ones, ls1, false);
+          ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][4], pb[g][ch][5]}, ones, ls0, false);
+          ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][6], pb[g][ch][7]}, ones, ls1, false);
         }
-        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][0], pb[ch][1]}, ones, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][2], pb[ch][3]}, ones, ls1, false);
-        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][4], pb[ch][5]}, ones, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[ch][6], pb[ch][7]}, ones, ls1, false);
+        ls[g] = ls0 + ls1;
       }
-      ls = ls0 + ls1;
     }
-    l_run += ls;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) l_run[g] += ls[g];
 
-    // ---- O^T += V^T P^T (16 keys per product); vector ALU: exponent form of
-    // tile t + 1's scores.  Slot j of half-wave h holds key 8 (j / 4) + 4 h +
-    // j % 4 of the chunk on both operands.
+    // ---- O^T += V^T P^T (16 keys per product, each V operand read feeding
+    // all NG groups); vector ALU: exponent form of tile t + 1's scores.  Slot
+    // j of half-wave h holds key 8 (j / 4) + 4 h + j % 4 of the chunk on both
+    // operands.
     const __bf16* vb = reinterpret_cast<const __bf16*>(v_lds[cur]);
 #pragma unroll
     for (int ch = 0; ch < kCH; ++ch)
@@ -412,20 +440,26 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
         const bf16x4 lo = lds_read_tr16(vp);
         const bf16x4 up = lds_read_tr16(vp + 8 * G::kOct * 8);
         const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-        acc[dt] = mfma32(a, pb[ch], acc[dt]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) acc[g][dt] = mfma32(a, pb[g][ch], acc[g][dt]);
       }
-    const float neg_m = -m_ref;
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt)
+    for (int g = 0; g < NG; ++g) {
+      const float neg_m = -m_ref[g];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_nxt[kt][r] = fmaf(s_nxt[kt][r], c2, neg_m);
+      for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_nxt[g][kt][r] = fmaf(s_nxt[g][kt][r], c2, neg_m);
+    }
 
     dma_wait();
     __syncthreads();
     if (has1) {
       mask_tail(s_nxt, (t + 1) * kBc);
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) s_cur[kt] = s_nxt[kt];
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int kt = 0; kt < kKT; ++kt) s_cur[g][kt] = s_nxt[g][kt];
     }
   };
 
@@ -438,58 +472,61 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void attn_fwd_bf16_kernel(
   }
   if (t < n_tiles) iteration(I0{}, t);
 
-  const float l_tot = sum_with_partner32(l_run);
-  if (my_q < Nq) {
-    // This block's partial: O_b = acc / l_tot, LSE_b = m_ref + log2 l_tot
-    // (log2 units).  MERGE folds it into the running (Out, LSE) of the row
-    // with the log-sum-exp identity; LSE = -inf there marks an empty
-    // accumulator whose O is not read.
-    const size_t lrow = (size_t)bh * Nq + my_q;
-    const float lse_b = m_ref + fast_log2(l_tot);
-    float wb = 1.f / l_tot, wa = 0.f, lse_new = lse_b;
-    bool has_a = false;
-    if constexpr (MERGE) {
-      const float la = LSE[lrow] * kLog2e;
-      has_a = la != -INFINITY;
-      if (has_a) {
-        const float m = fmaxf(la, lse_b);
-        const float ea = fast_exp2(la - m), eb = fast_exp2(lse_b - m);
-        const float inv = 1.f / (ea + eb);
-        wa = ea * inv;
-        wb = eb * inv / l_tot;
-        lse_new = m + fast_log2(ea + eb);
-      }
-    }
-    const size_t orow = lrow * D;
 #pragma unroll
-    for (int dt = 0; dt < G::kDTiles; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = dt * 32 + 8 * g + 4 * hi;
-        if (d0 < D) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[dt][4 * g + e] * wb;
-          if constexpr (OUT_F32) {
-            f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
-            if (MERGE && has_a) {
-              const f32x4 a = *p;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], o[e]);
-            }
-            *p = f32x4{o[0], o[1], o[2], o[3]};
-          } else {
-            bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
-            if (MERGE && has_a) {
-              const bf16x4 a = *p;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], o[e]);
-            }
-            *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-          }
+  for (int g = 0; g < NG; ++g) {
+    const float l_tot = sum_with_partner32(l_run[g]);
+    if (my_q[g] < Nq) {
+      // This block's partial: O_b = acc / l_tot, LSE_b = m_ref + log2 l_tot
+      // (log2 units).  MERGE folds it into the running (Out, LSE) of the row
+      // with the log-sum-exp identity; LSE = -inf there marks an empty
+      // accumulator whose O is not read.
+      const size_t lrow = (size_t)bh * Nq + my_q[g];
+      const float lse_b = m_ref[g] + fast_log2(l_tot);
+      float wb = 1.f / l_tot, wa = 0.f, lse_new = lse_b;
+      bool has_a = false;
+      if constexpr (MERGE) {
+        const float la = LSE[lrow] * kLog2e;
+        has_a = la != -INFINITY;
+        if (has_a) {
+          const float m = fmaxf(la, lse_b);
+          const float ea = fast_exp2(la - m), eb = fast_exp2(lse_b - m);
+          const float inv = 1.f / (ea + eb);
+          wa = ea * inv;
+          wb = eb * inv / l_tot;
+          lse_new = m + fast_log2(ea + eb);
         }
       }
-    if (hi == 0) LSE[lrow] = lse_new * kLn2;
+      const size_t orow = lrow * D;
+#pragma unroll
+      for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+          if (d0 < D) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = acc[g][dt][4 * q4 + e] * wb;
+            if constexpr (OUT_F32) {
+              f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
+              if (MERGE && has_a) {
+                const f32x4 a = *p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], o[e]);
+              }
+              *p = f32x4{o[0], o[1], o[2], o[3]};
+            } else {
+              bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
+              if (MERGE && has_a) {
+                const bf16x4 a = *p;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], o[e]);
+              }
+              *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+            }
+          }
+        }
+      if (hi == 0) LSE[lrow] = lse_new * kLn2;
+    }
   }
 }
 
@@ -501,7 +538,9 @@ template <int D>
 hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH,
                          int Nq, int Nkv, float scale, bool out_f32, bool merge,
                          hipStream_t stream) {
-  const int n_qtiles = (Nq + kBr - 1) / kBr;
+  constexpr int NG = kGroups;
+  constexpr int kRowsWG = (kThreads / 64) * 32 * NG;
+  const int n_qtiles = (Nq + kRowsWG - 1) / kRowsWG;
   const dim3 grid((unsigned)(n_qtiles * BH));
   const float c2 = scale * kLog2e;
   const __bf16* q = static_cast<const __bf16*>(Q);
@@ -509,14 +548,14 @@ hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, f
   const __bf16* v = static_cast<const __bf16*>(V);
   if (out_f32) {
     if (merge)
-      attn_fwd_bf16_kernel<D, true, true><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+      attn_fwd_bf16_kernel<D, NG, true, true><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
     else
-      attn_fwd_bf16_kernel<D, true, false><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+      attn_fwd_bf16_kernel<D, NG, true, false><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
   } else {
     if (merge)
-      attn_fwd_bf16_kernel<D, false, true><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+      attn_fwd_bf16_kernel<D, NG, false, true><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
     else
-      attn_fwd_bf16_kernel<D, false, false><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+      attn_fwd_bf16_kernel<D, NG, false, false><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
   }
   return hipGetLastError();
 }
