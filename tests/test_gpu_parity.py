@@ -361,3 +361,61 @@ def test_cfg_relmae_dit_xl_256_and_identity():
     assert abs(float(rm.item()) - want) <= 1e-5 * want
     assert float(rz.item()) == 0.0 and float(r00.item()) == 0.0
     assert_f32_close(to_f64(out), oracle.ref_cfg(to_oracle(w["eps_u"]), to_oracle(w["eps_c"]), w["s"]), "cfg")
+
+
+def test_graph_replays_match_eager():
+    """The ring fold (fused and unfused), the patch step and the CFG combine
+    captured in one HIP graph and replayed several times, with eager work and
+    synchronisations between replays, give the eager result every time (the
+    library launches kernels only: no memsets, no allocations)."""
+    q, k, v = inputs.attn_inputs(1, 4, 300, 3 * 200, 128, "bf16", seed=21)
+    q, k, v = dev(q), dev(k), dev(v)
+    blocks = [(k[:, :, i * 200:(i + 1) * 200].contiguous(), v[:, :, i * 200:(i + 1) * 200].contiguous())
+              for i in range(3)]
+    w = inputs.video_patch(N=600, Np=200, p0=200, H=4)
+    qp, kp, vp = dev(w["q_p"]), dev(w["k_p"]), dev(w["v_p"])
+    kb, vb = dev(w["k_buf"]), dev(w["v_buf"])
+    u, c = dev(torch.randn(5000)), dev(torch.randn(5000))
+    o_acc = torch.empty(1, 4, 300, 128, device="cuda:0")
+    l_acc = torch.empty(1, 4, 300, device="cuda:0")
+    o_f = torch.empty_like(o_acc)
+    l_f = torch.empty_like(l_acc)
+    o_t = torch.empty_like(o_acc)
+    l_t = torch.empty_like(l_acc)
+    o_p = torch.empty(1, 4, 200, 128, dtype=torch.bfloat16, device="cuda:0")
+    l_p = torch.empty(1, 4, 200, device="cuda:0")
+    cfg_out = torch.empty_like(u)
+
+    def step():
+        attn_block_fwd(q, *blocks[0], out=o_acc, lse=l_acc, out_dtype=torch.float32)
+        for kb_, vb_ in blocks[1:]:
+            attn_block_fwd(q, kb_, vb_, out=o_t, lse=l_t, out_dtype=torch.float32)
+            attn_lse_merge(o_acc, l_acc, o_t, l_t)
+        l_f.fill_(-float("inf"))
+        for kb_, vb_ in blocks:
+            attn_block_fwd_merge(q, kb_, vb_, o_f, l_f)
+        attn_patch_fwd(qp, kp, vp, kb, vb, w["p0"], out=o_p, lse=l_p)
+        cfg_combine(u, c, 4.0, out=cfg_out)
+
+    say("case graph capture")
+    step()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (o_acc, l_acc, o_f, l_f, o_p, l_p, cfg_out)]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (o_acc, l_acc, o_f, l_f, o_p, l_p, cfg_out):
+            t.zero_()                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (o_acc, l_acc, o_f, l_f, o_p, l_p, cfg_out)
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager result"
