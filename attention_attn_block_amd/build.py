@@ -1,7 +1,9 @@
 """Build libdit_attn.so in-tree for gfx950 with hipcc.
 
 Each ``csrc/*.hip`` file compiles to an object in ``_build/`` (in parallel),
-then one shared library is linked next to this file.  Always recompiles.
+then one shared library is linked next to this file.  The plain-C client of
+the ABI in ``tests/abi_client.c`` is then compiled with the host C compiler
+and linked against that library.  Always recompiles.
 
     python -m attention_attn_block_amd.build
 """
@@ -18,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdit_attn.so")
 ARCH = "gfx950"
+CLIENT_SRC = os.path.join(ROOT, "tests", "abi_client.c")
+CLIENT = os.path.join(ROOT, "tests", "abi_client")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 # Packed-fp32 VALU forms are disabled for all device code.
 FLAGS = [
@@ -58,7 +63,26 @@ def build(verbose=False, jobs=None):
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    if os.path.exists(CLIENT_SRC):
+        build_client(verbose)
     return LIB
+
+
+def build_client(verbose=False):
+    """Compile the C client of the ABI (C11, no HIP device code): it includes
+    only include/dit_attn.h and links libdit_attn.so plus the HIP runtime."""
+    cc = os.environ.get("CC") or shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        raise RuntimeError("no host C compiler found for tests/abi_client.c")
+    tmp = CLIENT + ".tmp"
+    _run([cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          "-I", os.path.join(ROCM, "include"), CLIENT_SRC, "-o", tmp,
+          "-L", HERE, "-ldit_attn", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN/../attention_attn_block_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")])
+    os.replace(tmp, CLIENT)
+    if verbose:
+        print("built", CLIENT)
+    return CLIENT
 
 
 if __name__ == "__main__":

@@ -1,0 +1,69 @@
+"""The C ABI driven from a plain C program (tests/abi_client.c, built beside the
+library): no Python binding in the loop.  The CPU tests check that the client
+links against libdit_attn.so and rejects bad input before any HIP call; the GPU
+test runs full attention and both block folds (separate merge, fused merge)
+through it and compares every output with the fp64 oracle."""
+
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from attention_attn_block_amd import inputs
+from tests.gpu_util import assert_bf16_close, to_oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CLIENT = os.path.join(ROOT, "tests", "abi_client")
+
+
+def client():
+    assert os.path.exists(CLIENT), "tests/abi_client is not built (python -m attention_attn_block_amd.build)"
+    return CLIENT
+
+
+def test_client_resolves_the_library():
+    out = subprocess.run(["ldd", client()], capture_output=True, text=True).stdout
+    line = [l for l in out.splitlines() if "libdit_attn.so" in l]
+    assert line and "not found" not in line[0], out
+
+
+def test_client_rejects_bad_input(tmp_path):
+    assert subprocess.run([client()], capture_output=True).returncode == 2
+    missing = tmp_path / "missing.bin"
+    assert subprocess.run([client(), str(missing), str(tmp_path / "o")],
+                          capture_output=True).returncode == 2
+    bad = tmp_path / "bad.bin"
+    # nblocks (4) > Nkv (3): refused while parsing, before any HIP call
+    bad.write_bytes(np.array([1, 1, 2, 3, 64, 4], np.int32).tobytes() + np.float32(0.1).tobytes())
+    assert subprocess.run([client(), str(bad), str(tmp_path / "o")],
+                          capture_output=True).returncode == 2
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape", [(1, 3, 300, 777, 128, 3), (2, 2, 129, 200, 72, 2)])
+def test_c_client_matches_oracle(tmp_path, shape):
+    B, H, Nq, Nkv, d, nb = shape
+    print("case c-client", shape, flush=True)
+    q, k, v = inputs.attn_inputs(B, H, Nq, Nkv, d, "bf16", seed=31 + d)
+    scale = inputs.default_scale(d)
+    qb, kb, vb = to_oracle(q), to_oracle(k), to_oracle(v)
+    fin, fout = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(fin, "wb") as f:
+        f.write(np.array([B, H, Nq, Nkv, d, nb], np.int32).tobytes())
+        f.write(np.float32(scale).tobytes())
+        for a in (qb, kb, vb):
+            f.write(np.ascontiguousarray(a).tobytes())
+    p = subprocess.run(["timeout", "-k", "10", "120", client(), str(fin), str(fout)],
+                       capture_output=True, text=True)
+    assert p.returncode == 0, p.stdout + p.stderr
+    raw = np.fromfile(fout, np.float32)
+    no, nl = B * H * Nq * d, B * H * Nq
+    assert raw.size == 3 * (no + nl)
+    Or, Lr = oracle.ref_attn(qb, kb, vb, scale)
+    for r, what in enumerate(("full", "block fold", "fused block fold")):
+        o = raw[r * (no + nl): r * (no + nl) + no].reshape(B, H, Nq, d)
+        l = raw[r * (no + nl) + no: (r + 1) * (no + nl)].reshape(B, H, Nq)
+        assert_bf16_close(o.astype(np.float64), Or, f"c-client {what} O")
+        assert_bf16_close(l.astype(np.float64), Lr, f"c-client {what} LSE")
