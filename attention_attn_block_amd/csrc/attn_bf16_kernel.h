@@ -28,7 +28,9 @@
 //    ds_read_b64_tr_b16.
 //  * The key loop is software-pipelined with K one tile ahead of V: while the
 //    vector ALU turns tile t's scores into weights, the matrix cores already
-//    compute tile t+1's scores; one barrier per tile.
+//    compute tile t+1's scores; one barrier per tile.  Inside a tile the LDS
+//    operand reads run several products ahead of the products that use them
+//    (kKDepth, kVDepth), so LDS latency overlaps matrix work.
 //  * Workgroup ids are remapped so that all query tiles of a head run on the
 //    same XCD (ids are dealt round-robin over the 8 XCDs), sharing that XCD's
 //    L2 for the head's K/V stream.
@@ -64,6 +66,12 @@ constexpr int kKT = kBc / 32;   // 32-key score accumulators per tile
 constexpr int kCH = kBc / 16;   // 16-key chunks of the PV product per tile
 constexpr int kWavesPerSimd = 2;  // with one query group per wave
 constexpr int kGroups = 1;        // query groups of 32 rows per wave
+// Software prefetch: K-operand LDS reads issued this many score products
+// ahead of their use, V-operand reads this many PV products ahead; vector
+// instructions placed after each score product.
+constexpr int kKDepth = 4;
+constexpr int kVDepth = 2;
+constexpr int kQkValu = 6;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -218,18 +226,12 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // i the unit 64 (4j + w) + i; the unit stored there is row p / kOct, stored
   // column p % kOct, which holds global column (p % kOct) ^ swz(row).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  int kg_off[G::kKLoads], vg_off[G::kKLoads], g_row[G::kKLoads];
-#pragma unroll
-  for (int j = 0; j < G::kKLoads; ++j) {
-    const int pu = tid + kThreads * j;
-    const int row = pu / G::kOct, col = pu - row * G::kOct;
-    g_row[j] = row;
-    kg_off[j] = row * D + 8 * (col ^ swz_k<G::kOct>(row));
-    vg_off[j] = row * D + 8 * (col ^ swz_v<G::kOct>(row));
-  }
-  auto dma_tile = [&](const __bf16* base, const int* goff, u32x4* lds, int kv0) {
-    const __bf16* tb = base + (size_t)kv0 * D;
-    const bool full = kv0 + kBc <= Nkv;
+  // Rows past the block (ragged last tile) are clamped to its last row,
+  // without a branch; the 32-bit byte offset lets the load use a scalar base.
+  auto dma_tile = [&](auto is_v, const __bf16* base, u32x4* lds, int kv0) {
+    constexpr bool kV = decltype(is_v)::value;
+    const char* tb = reinterpret_cast<const char*>(base + (size_t)kv0 * D);
+    const int lim = Nkv - 1 - kv0;
 #pragma unroll
     for (int j = 0; j < G::kKLoads; ++j) {
       const int first_unit = 64 * ((kThreads / 64) * j + wv);
@@ -237,17 +239,19 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       // number of 64-unit wave loads, the lanes past its end must not load.
       const bool lane_in = (kTileUnits % 64 == 0) || tid + kThreads * j < kTileUnits;
       if (first_unit < kTileUnits && lane_in) {
-        int off = goff[j];
-        if (!full) {  // ragged last tile: clamp rows into the block
-          const int over = kv0 + g_row[j] - (Nkv - 1);
-          off -= over > 0 ? over * D : 0;
-        }
+        const int pu = tid + kThreads * j;
+        const int row = pu / G::kOct, col = pu - row * G::kOct;
+        const int sw = kV ? swz_v<G::kOct>(row) : swz_k<G::kOct>(row);
+        const int rc = row < lim ? row : lim;
+        const unsigned off = (unsigned)(rc * D + 8 * (col ^ sw)) * 2u;
         __builtin_amdgcn_global_load_lds(
             (const void*)(tb + off),
             (__attribute__((address_space(3))) void*)(lds + first_unit), 16, 0, 0);
       }
     }
   };
+  using IsK = std::integral_constant<bool, false>;
+  using IsV = std::integral_constant<bool, true>;
   // All of this wave's tile loads have landed in LDS (before a barrier).
   auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -261,11 +265,13 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // operand read feeds the products of all NG query groups.
   auto qk = [&](int buf, f32x16 (*s)[kKT]) {
 #pragma unroll
-    for (int kt = 0; kt < kKT; ++kt) {
+    for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
       for (int g = 0; g < NG; ++g) s[g][kt] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < G::kChunks; ++c) {
+    for (int c = 0; c < G::kChunks; ++c) {
+#pragma unroll
+      for (int kt = 0; kt < kKT; ++kt) {
         bf16x8 a;
         if (G::kHalfTail && c == G::kChunks - 1 && hi) {
           a = bf16x8{};
@@ -320,14 +326,17 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // runs on the vector ALU, the matrix cores compute S for tile t + 1.  LDS:
   // K(t) and V(t) live in buffer t % 2.  Iteration t reads K(t+1) and V(t);
   // its loads of K(t+2) and V(t+1) land in the buffers iteration t-1 freed.
-  dma_tile(Kh, kg_off, k_lds[0], 0);
-  dma_tile(Vh, vg_off, v_lds[0], 0);
-  if (n_tiles > 1) dma_tile(Kh, kg_off, k_lds[1], kBc);
+  dma_tile(IsK{}, Kh, k_lds[0], 0);
+  dma_tile(IsV{}, Vh, v_lds[0], 0);
+  if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kBc);
   dma_wait();
   __syncthreads();
 
   f32x16 s_cur[NG][kKT];
   qk(0, s_cur);
+  // Iteration 0 loads K tile 2 into the buffer tile 0 was just read from:
+  // every wave must have finished those reads first.
+  __syncthreads();
   mask_tail(s_cur, 0);
   // Reference max from tile 0; s_cur then holds the exponent form
   // t = s * scale * log2(e) - m_ref.
@@ -346,14 +355,38 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     constexpr int cur = decltype(buf_c)::value;  // = t % 2
     constexpr int nxt = cur ^ 1;
     const bool has1 = t + 1 < n_tiles, has2 = t + 2 < n_tiles;
-    if (has2) dma_tile(Kh, kg_off, k_lds[cur], (t + 2) * kBc);
-    if (has1) dma_tile(Vh, vg_off, v_lds[nxt], (t + 1) * kBc);
+    if (has2) dma_tile(IsK{}, Kh, k_lds[cur], (t + 2) * kBc);
+    if (has1) dma_tile(IsV{}, Vh, v_lds[nxt], (t + 1) * kBc);
 
     // ---- matrix cores: S for tile t + 1; vector ALU: weights of tile t ----
     // (Branch-free so the two interleave.  On the last tile the product reads
-    // an allocated, unused K buffer and its result is dropped.)
+    // an allocated, unused K buffer and its result is dropped.)  K-operand
+    // reads run kKD products ahead of their use: each product's operand read
+    // is issued as a value of its own, and the scheduling groups below fix
+    // the order read, product, vector work.  The two 32-key accumulators
+    // alternate so consecutive products are independent.
     f32x16 s_nxt[NG][kKT];
-    qk(nxt, s_nxt);
+    constexpr int kQK = kKT * G::kChunks;
+    constexpr int kKD = kKDepth;
+    bf16x8 kr[kQK];
+    auto kread = [&](int i) -> bf16x8 {
+      const int c = i / kKT, kt = i % kKT;
+      if (G::kHalfTail && c == G::kChunks - 1 && hi) return bf16x8{};
+      return __builtin_bit_cast(bf16x8, k_lds[nxt][kt * 32 * G::kOct + k_unit[c]]);
+    };
+#pragma unroll
+    for (int i = 0; i < kKD && i < kQK; ++i) kr[i] = kread(i);
+    __builtin_amdgcn_sched_group_barrier(0x100, kKD, 0);
+#pragma unroll
+    for (int i = 0; i < kQK; ++i) {
+      if (i + kKD < kQK) kr[i + kKD] = kread(i + kKD);
+      const int c = i / kKT, kt = i % kKT;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s_nxt[g][kt] = mfma32(kr[i], qf[g][c], c == 0 ? f32x16{} : s_nxt[g][kt]);
+      if (i + kKD < kQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, kQkValu, 0);  // VALU
+    }
 
     bf16x8 pb[NG][kCH];
     float ls[NG];
@@ -375,16 +408,6 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
         ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][6], pb[g][ch][7]}, ones, ls1, false);
       }
       ls[g] = ls0 + ls1;
-    }
-    // Issue order for this block: K-operand LDS reads two reads ahead, then
-    // per read the NG products it feeds and a share of the softmax VALU work,
-    // so the vector ALU runs while the matrix core is busy.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // LDS read
-#pragma unroll
-    for (int i = 0; i < kKT * G::kChunks; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 32 * kKT * NG / G::kChunks, 0);  // VALU
     }
 
     // Rare: a lane's share of a row's sum exceeds the limit (so some weight
@@ -430,26 +453,41 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     // ---- O^T += V^T P^T (16 keys per product, each V operand read feeding
     // all NG groups); vector ALU: exponent form of tile t + 1's scores.  Slot
     // j of half-wave h holds key 8 (j / 4) + 4 h + j % 4 of the chunk on both
-    // operands.
+    // operands.  The two transposing reads of a product are issued kVD
+    // products ahead; each product is followed by its share of the
+    // exponent-form arithmetic.
     const __bf16* vb = reinterpret_cast<const __bf16*>(v_lds[cur]);
+    constexpr int kPV = kCH * G::kDTiles;
+    constexpr int kVD = kVDepth;
+    constexpr int kSV = kKT * 16;  // exponent-form values per group
+    bf16x8 vr[kPV];
+    auto vread = [&](int j) -> bf16x8 {
+      const int ch = j / G::kDTiles, dt = j % G::kDTiles;
+      const __bf16* vp = vb + v_off[dt] + 16 * ch * G::kOct * 8;
+      const bf16x4 lo = lds_read_tr16(vp);
+      const bf16x4 up = lds_read_tr16(vp + 8 * G::kOct * 8);
+      return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+    };
+    float neg_m[NG];
 #pragma unroll
-    for (int ch = 0; ch < kCH; ++ch)
+    for (int g = 0; g < NG; ++g) neg_m[g] = -m_ref[g];
 #pragma unroll
-      for (int dt = 0; dt < G::kDTiles; ++dt) {
-        const __bf16* vp = vb + v_off[dt] + 16 * ch * G::kOct * 8;
-        const bf16x4 lo = lds_read_tr16(vp);
-        const bf16x4 up = lds_read_tr16(vp + 8 * G::kOct * 8);
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+    for (int j = 0; j < kVD && j < kPV; ++j) vr[j] = vread(j);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVD, 1);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) acc[g][dt] = mfma32(a, pb[g][ch], acc[g][dt]);
-      }
+    for (int j = 0; j < kPV; ++j) {
+      if (j + kVD < kPV) vr[j + kVD] = vread(j + kVD);
+      const int ch = j / G::kDTiles, dt = j % G::kDTiles;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const float neg_m = -m_ref[g];
+      for (int g = 0; g < NG; ++g) acc[g][dt] = mfma32(vr[j], pb[g][ch], acc[g][dt]);
 #pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s_nxt[g][kt][r] = fmaf(s_nxt[g][kt][r], c2, neg_m);
+        for (int e = j * kSV / kPV; e < (j + 1) * kSV / kPV; ++e)
+          s_nxt[g][e / 16][e % 16] = fmaf(s_nxt[g][e / 16][e % 16], c2, neg_m[g]);
+      if (j + kVD < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, NG, 1);      // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2 * NG, 1);  // VALU
     }
 
     dma_wait();
