@@ -71,7 +71,7 @@ constexpr int kGroups = 1;        // query groups of 32 rows per wave
 // instructions placed after each score product.
 constexpr int kKDepth = 4;
 constexpr int kVDepth = 2;
-constexpr int kQkValu = 6;
+constexpr int kQkValu = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -230,15 +230,24 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // without a branch; the 32-bit byte offset lets the load use a scalar base.
   auto dma_tile = [&](auto is_v, const __bf16* base, u32x4* lds, int kv0) {
     constexpr bool kV = decltype(is_v)::value;
-    const char* tb = reinterpret_cast<const char*>(base + (size_t)kv0 * D);
+    // The tile base is one scalar address (so each load is scalar base +
+    // 32-bit lane offset); the halves come back from readfirstlane as int
+    // and are widened as unsigned.  The wave index is re-read here so the LDS
+    // destinations are recomputed per tile instead of held in registers.
+    const uint64_t tba = reinterpret_cast<uint64_t>(base + (size_t)kv0 * D);
+    const char* tb = reinterpret_cast<const char*>(
+        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tba >> 32)) << 32) |
+        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tba));
+    int wvl = wv;
+    asm volatile("" : "+s"(wvl));
     const int lim = Nkv - 1 - kv0;
 #pragma unroll
     for (int j = 0; j < G::kKLoads; ++j) {
-      const int first_unit = 64 * ((kThreads / 64) * j + wv);
+      const int first_unit = 64 * ((kThreads / 64) * j + wvl);
       // Wave-uniform skip of loads past the tile; when the tile is not a whole
       // number of 64-unit wave loads, the lanes past its end must not load.
       const bool lane_in = (kTileUnits % 64 == 0) || tid + kThreads * j < kTileUnits;
-      if (first_unit < kTileUnits && lane_in) {
+      if (kTileUnits % kThreads == 0 || (first_unit < kTileUnits && lane_in)) {
         const int pu = tid + kThreads * j;
         const int row = pu / G::kOct, col = pu - row * G::kOct;
         const int sw = kV ? swz_v<G::kOct>(row) : swz_k<G::kOct>(row);
