@@ -72,6 +72,9 @@ constexpr int kGroups = 1;        // query groups of 32 rows per wave
 constexpr int kKDepth = 4;
 constexpr int kVDepth = 2;
 constexpr int kQkValu = 4;
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs: 32-bit
+// data format; out-of-range reads return zero.
+constexpr int kBufferFlags = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -226,36 +229,45 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // i the unit 64 (4j + w) + i; the unit stored there is row p / kOct, stored
   // column p % kOct, which holds global column (p % kOct) ^ swz(row).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // Rows past the block (ragged last tile) are clamped to its last row,
-  // without a branch; the 32-bit byte offset lets the load use a scalar base.
+  // Byte offsets of this lane's unit inside a full K / V tile (fixed for the
+  // whole key loop).
+  unsigned koff[G::kKLoads], voff[G::kKLoads];
+#pragma unroll
+  for (int j = 0; j < G::kKLoads; ++j) {
+    const int pu = tid + kThreads * j;
+    const int row = pu / G::kOct, col = pu - row * G::kOct;
+    koff[j] = (unsigned)(row * D + 8 * (col ^ swz_k<G::kOct>(row))) * 2u;
+    voff[j] = (unsigned)(row * D + 8 * (col ^ swz_v<G::kOct>(row))) * 2u;
+  }
+  // One tile, as buffer loads against a resource that covers exactly the
+  // tile's rows inside the block: in the ragged last tile the rows past the
+  // block fall outside the resource, are not read, and land in LDS as zeros
+  // (their keys are masked).
   auto dma_tile = [&](auto is_v, const __bf16* base, u32x4* lds, int kv0) {
     constexpr bool kV = decltype(is_v)::value;
-    // The tile base is one scalar address (so each load is scalar base +
-    // 32-bit lane offset); the halves come back from readfirstlane as int
-    // and are widened as unsigned.  The wave index is re-read here so the LDS
-    // destinations are recomputed per tile instead of held in registers.
+    // The tile base is one scalar address; the halves come back from
+    // readfirstlane as int and are widened as unsigned.  The wave index is
+    // re-read here so the LDS destinations are recomputed per tile instead of
+    // held in registers.
     const uint64_t tba = reinterpret_cast<uint64_t>(base + (size_t)kv0 * D);
-    const char* tb = reinterpret_cast<const char*>(
+    const void* tb = reinterpret_cast<const void*>(
         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tba >> 32)) << 32) |
         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tba));
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(tb), (short)0, (Nkv - kv0 < kBc ? Nkv - kv0 : kBc) * D * 2, kBufferFlags);
     int wvl = wv;
     asm volatile("" : "+s"(wvl));
-    const int lim = Nkv - 1 - kv0;
 #pragma unroll
     for (int j = 0; j < G::kKLoads; ++j) {
       const int first_unit = 64 * ((kThreads / 64) * j + wvl);
-      // Wave-uniform skip of loads past the tile; when the tile is not a whole
-      // number of 64-unit wave loads, the lanes past its end must not load.
+      // Wave-uniform skip of loads past the tile; when the tile is not a
+      // whole number of 64-unit wave loads, the lanes past its end must not
+      // load.
       const bool lane_in = (kTileUnits % 64 == 0) || tid + kThreads * j < kTileUnits;
       if (kTileUnits % kThreads == 0 || (first_unit < kTileUnits && lane_in)) {
-        const int pu = tid + kThreads * j;
-        const int row = pu / G::kOct, col = pu - row * G::kOct;
-        const int sw = kV ? swz_v<G::kOct>(row) : swz_k<G::kOct>(row);
-        const int rc = row < lim ? row : lim;
-        const unsigned off = (unsigned)(rc * D + 8 * (col ^ sw)) * 2u;
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(tb + off),
-            (__attribute__((address_space(3))) void*)(lds + first_unit), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(lds + first_unit), 16,
+            (int)(kV ? voff[j] : koff[j]), 0, 0, 0);
       }
     }
   };
