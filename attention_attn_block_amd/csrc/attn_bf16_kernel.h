@@ -513,13 +513,14 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 
     dma_wait();
     __syncthreads();
-    if (has1) {
-      mask_tail(s_nxt, (t + 1) * kBc);
+    // Unconditional (after the last tile the values are simply unused), so
+    // the exponent-form arithmetic above stays interleaved with the PV
+    // products instead of being sunk past the barrier.
+    mask_tail(s_nxt, (t + 1) * kBc);
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
-        for (int kt = 0; kt < kKT; ++kt) s_cur[g][kt] = s_nxt[g][kt];
-    }
+      for (int kt = 0; kt < kKT; ++kt) s_cur[g][kt] = s_nxt[g][kt];
   };
 
   using I0 = std::integral_constant<int, 0>;
