@@ -22,7 +22,7 @@
 //    the keys inside each 16-key chunk are visited in the order the
 //    accumulator holds them.
 //  * K and V tiles of 64 keys move from HBM straight into LDS with
-//    global_load_lds_dwordx4 (no staging registers), double-buffered, in
+//    buffer_load_dwordx4 ... lds (no staging registers), double-buffered, in
 //    16-byte units swizzled so that both LDS read patterns are bank-conflict
 //    free.  V stays row-major; the PV operand is read with the transposing
 //    ds_read_b64_tr_b16.
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     }
   }
 
-  // Tile staging: global -> LDS directly (global_load_lds_dwordx4, no
+  // Tile staging: global -> LDS directly (buffer_load_dwordx4 ... lds, no
   // registers).  Wave w's j-th load writes LDS units 64 (4j + w) .. +63, lane
   // i the unit 64 (4j + w) + i; the unit stored there is row p / kOct, stored
   // column p % kOct, which holds global column (p % kOct) ^ swz(row).
