@@ -179,6 +179,27 @@ def test_large_scores_stay_finite():
     check_attn(q, k, v, 0.125, torch.float32, "peaked scores")
 
 
+@pytest.mark.parametrize("Nkv", [30, 100, 1000])
+def test_ragged_tile_ignores_stale_lds(Nkv):
+    """Key rows past a ragged last tile must not carry over whatever an earlier
+    kernel left in LDS.  A first call over all-NaN K/V fills every CU's tile
+    buffers with NaN bit patterns; a ragged call right after on the same
+    stream must still match the oracle (a stale NaN V row would turn the
+    zero weight of a masked key into NaN)."""
+    say("case stale-LDS ragged Nkv", Nkv)
+    nan = torch.full((1, 32, 4096, 128), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    q0 = torch.zeros(1, 32, 4096, 128, dtype=torch.bfloat16, device="cuda:0")
+    q, k, v = inputs.attn_inputs(1, 4, 300, Nkv, 128, "bf16", seed=40 + Nkv)
+    gq, gk, gv = dev(q), dev(k), dev(v)
+    scale = inputs.default_scale(128)
+    attn_block_fwd(q0, nan, nan, scale=scale)          # result discarded
+    O, L = attn_block_fwd(gq, gk, gv, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale)
+    assert_bf16_close(to_f64(O), Or, f"stale-LDS Nkv={Nkv} O")
+    assert_bf16_close(to_f64(L), Lr, f"stale-LDS Nkv={Nkv} LSE")
+
+
 def test_merge_edge_cases():
     rows, d = 300, 72
     g = torch.Generator().manual_seed(9)
