@@ -167,11 +167,10 @@ __device__ __forceinline__ float row_max(const f32x16* s) {
   return mx;
 }
 
-// NG = query groups of 32 rows per wave.  NG = 2 lets every K and V operand
-// read from LDS (and every tile loaded into LDS) feed twice the matrix work,
-// but its registers (with 32-key tiles; 64-key tiles spill) allow only one
-// wave per SIMD, and on MI355X that ran about a third slower than NG = 1 with
-// two waves per SIMD, so kGroups is 1.
+// NG = query groups of 32 rows per wave.  NG = 2 would let every K and V
+// operand read from LDS (and every tile loaded into LDS) feed twice the
+// matrix work, but it needs one wave per SIMD and about 512 registers, and the
+// compiler then spills heavily; kGroups is 1.
 template <int D, int NG, bool OUT_F32, bool MERGE>
 __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
