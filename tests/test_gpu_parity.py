@@ -143,6 +143,23 @@ def test_video_patch_full_size_sampled_rows():
     assert_bf16_close(to_f64(L[:, :, rows]), Lr, "video_patch LSE (sampled rows)")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_long_ragged_block_sampled_rows(out_dtype):
+    """A long KV block whose length is not a multiple of the 64-key tile
+    (40 037 keys: 625 full tiles and a 37-row tail) and a ragged query count,
+    at the video workload's d = 128: sampled query rows against the oracle."""
+    B, H, Nq, Nkv, d = 1, 3, 1000, 40037, 128
+    say("case long ragged block", (B, H, Nq, Nkv, d), out_dtype)
+    q, k, v = inputs.attn_inputs(B, H, Nq, Nkv, d, "bf16", seed=77)
+    scale = inputs.default_scale(d)
+    O, L = run_attn(q, k, v, scale, out_dtype)
+    rng = np.random.default_rng(78)
+    rows = np.unique(np.concatenate([[0, 127, 128, 999], rng.choice(Nq, 60, replace=False)]))
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale, rows=rows)
+    assert_bf16_close(to_f64(O[:, :, rows]), Or, "long ragged block O (sampled rows)")
+    assert_bf16_close(to_f64(L[:, :, rows]), Lr, "long ragged block LSE (sampled rows)")
+
+
 # ---------------------------------------------------------------------------
 # Edge cases: ragged tiles, odd head dims, tiny and degenerate sizes
 # ---------------------------------------------------------------------------
