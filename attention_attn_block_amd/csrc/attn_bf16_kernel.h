@@ -11,8 +11,9 @@
 // rescaled whenever the maximum grows, so each KV tile is read once.
 //
 // Work decomposition (CDNA4, wave64):
-//  * A workgroup owns 128 query rows of one (batch, head); each of its four
-//    waves owns 32 rows for the whole key loop.
+//  * A workgroup owns 256 query rows of one (batch, head); each of its eight
+//    waves owns 32 rows for the whole key loop.  Waves w and w + 4 share a
+//    SIMD (two waves per SIMD, one workgroup per CU).
 //  * Both contractions run on v_mfma_f32_32x32x16_bf16 in the transposed
 //    form S^T = K Q^T and O^T = V^T P^T.  In the 32x32 accumulator layout a
 //    lane then holds 16 values of ONE query row (column = lane % 32), so the
@@ -26,11 +27,14 @@
 //    16-byte units swizzled so that both LDS read patterns are bank-conflict
 //    free.  V stays row-major; the PV operand is read with the transposing
 //    ds_read_b64_tr_b16.
-//  * The key loop is software-pipelined with K one tile ahead of V: while the
-//    vector ALU turns tile t's scores into weights, the matrix cores already
-//    compute tile t+1's scores; one barrier per tile.  Inside a tile the LDS
-//    operand reads run several products ahead of the products that use them
-//    (kKDepth, kVDepth), so LDS latency overlaps matrix work.
+//  * Ping-pong: each wave alternates a matrix phase (tile t+1's scores and
+//    tile t's PV product, K one tile ahead of V) with a vector phase (tile
+//    t+1's weights), and the two waves of a SIMD run these phases half a tile
+//    apart, separated by workgroup barriers, so one wave's softmax runs while
+//    the other keeps the matrix core busy.  The wave group in its vector
+//    phase also issues the tile loads.  Inside the matrix phase the LDS
+//    operand reads run several products ahead of their use (kKDepth,
+//    kVDepth).
 //  * Workgroup ids are remapped so that all query tiles of a head run on the
 //    same XCD (ids are dealt round-robin over the 8 XCDs), sharing that XCD's
 //    L2 for the head's K/V stream.
@@ -60,18 +64,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;   // 4 waves
+constexpr int kThreads = 512;   // 8 waves: two per SIMD, ping-pong
+constexpr int kDmaThreads = 256;  // the tile loads are issued by one group of 4 waves
 constexpr int kBc = 64;         // keys per KV tile (a multiple of 32)
 constexpr int kKT = kBc / 32;   // 32-key score accumulators per tile
 constexpr int kCH = kBc / 16;   // 16-key chunks of the PV product per tile
 constexpr int kWavesPerSimd = 2;  // with one query group per wave
 constexpr int kGroups = 1;        // query groups of 32 rows per wave
 // Software prefetch: K-operand LDS reads issued this many score products
-// ahead of their use, V-operand reads this many PV products ahead; vector
-// instructions placed after each score product.
+// ahead of their use, V-operand reads this many PV products ahead.
 constexpr int kKDepth = 4;
 constexpr int kVDepth = 2;
-constexpr int kQkValu = 4;
 // Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs: 32-bit
 // data format; out-of-range reads return zero.
 constexpr int kBufferFlags = 0x00020000;
@@ -85,7 +88,7 @@ struct Geo {
   static constexpr int kDTiles = (D + 31) / 32;     // 32-row tiles of O^T
   static constexpr int kOct = D / 8;                // 16-byte groups per row in memory
   static constexpr int kKItems = kBc * kOct;        // 16-byte K (or V) groups per tile
-  static constexpr int kKLoads = (kKItems + kThreads - 1) / kThreads;
+  static constexpr int kKLoads = (kKItems + kDmaThreads - 1) / kDmaThreads;
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -170,7 +173,8 @@ __device__ __forceinline__ float row_max(const f32x16* s) {
 // NG = query groups of 32 rows per wave.  NG = 2 would let every K and V
 // operand read from LDS (and every tile loaded into LDS) feed twice the
 // matrix work, but it needs one wave per SIMD and about 512 registers, and the
-// compiler then spills heavily; kGroups is 1.
+// compiler then spills heavily; kGroups is 1 (the ping-pong schedule also
+// assumes one group).
 template <int D, int NG, bool OUT_F32, bool MERGE>
 __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -227,13 +231,14 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // registers).  Wave w's j-th load writes LDS units 64 (4j + w) .. +63, lane
   // i the unit 64 (4j + w) + i; the unit stored there is row p / kOct, stored
   // column p % kOct, which holds global column (p % kOct) ^ swz(row).
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wv = __builtin_amdgcn_readfirstlane(wave & 3);
+  const int dtid = tid & (kDmaThreads - 1);
   // Byte offsets of this lane's unit inside a full K / V tile (fixed for the
   // whole key loop).
   unsigned koff[G::kKLoads], voff[G::kKLoads];
 #pragma unroll
   for (int j = 0; j < G::kKLoads; ++j) {
-    const int pu = tid + kThreads * j;
+    const int pu = dtid + kDmaThreads * j;
     const int row = pu / G::kOct, col = pu - row * G::kOct;
     koff[j] = (unsigned)(row * D + 8 * (col ^ swz_k<G::kOct>(row))) * 2u;
     voff[j] = (unsigned)(row * D + 8 * (col ^ swz_v<G::kOct>(row))) * 2u;
@@ -258,12 +263,12 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     asm volatile("" : "+s"(wvl));
 #pragma unroll
     for (int j = 0; j < G::kKLoads; ++j) {
-      const int first_unit = 64 * ((kThreads / 64) * j + wvl);
+      const int first_unit = 64 * ((kDmaThreads / 64) * j + wvl);
       // Wave-uniform skip of loads past the tile; when the tile is not a
       // whole number of 64-unit wave loads, the lanes past its end must not
       // load.
-      const bool lane_in = (kTileUnits % 64 == 0) || tid + kThreads * j < kTileUnits;
-      if (kTileUnits % kThreads == 0 || (first_unit < kTileUnits && lane_in)) {
+      const bool lane_in = (kTileUnits % 64 == 0) || dtid + kDmaThreads * j < kTileUnits;
+      if (kTileUnits % kDmaThreads == 0 || (first_unit < kTileUnits && lane_in)) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsrc, (__attribute__((address_space(3))) void*)(lds + first_unit), 16,
             (int)(kV ? voff[j] : koff[j]), 0, 0, 0);
@@ -342,73 +347,49 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   const int n_tiles = (Nkv + kBc - 1) / kBc;
 
-  // Software pipeline: K runs one tile ahead of V.  While tile t's softmax
-  // runs on the vector ALU, the matrix cores compute S for tile t + 1.  LDS:
-  // K(t) and V(t) live in buffer t % 2.  Iteration t reads K(t+1) and V(t);
-  // its loads of K(t+2) and V(t+1) land in the buffers iteration t-1 freed.
-  dma_tile(IsK{}, Kh, k_lds[0], 0);
-  dma_tile(IsV{}, Vh, v_lds[0], 0);
-  if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kBc);
+  // Ping-pong schedule.  Waves w and w + 4 share a SIMD.  Group A (waves 0-3)
+  // and group B (waves 4-7) run the same per-wave pipeline one slot apart, so
+  // while one wave of a SIMD is in its matrix phase the other is in its vector
+  // phase.  Per tile t a wave runs
+  //   M(t):   S(t+1) = K(t+1) Q^T and O^T += V(t)^T P(t)^T  (matrix cores, LDS)
+  //   W(t+1): exponent form, weights P(t+1), normaliser, rare rescale  (VALU)
+  // Group A runs M(k) in slot 2k and W(k+1) in slot 2k+1; group B runs M(k) in
+  // slot 2k+1 and W(k+1) in slot 2k+2.  Every slot ends with a barrier that
+  // every wave executes (the slot count is the same for the whole workgroup).
+  // K(t) and V(t) live in LDS buffer t % 2.  Slot 2k starts the loads of
+  // K(k+2) and V(k+1) into the buffers whose last readers ran in slot 2k-1;
+  // slot 2k+1 ends by waiting for them.
+  const int grp = wave >> 2;
+  if (grp == 1) {
+    dma_tile(IsK{}, Kh, k_lds[0], 0);
+    dma_tile(IsV{}, Vh, v_lds[0], 0);
+    if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kBc);
+  }
   dma_wait();
   __syncthreads();
 
-  f32x16 s_cur[NG][kKT];
-  qk(0, s_cur);
-  // Iteration 0 loads K tile 2 into the buffer tile 0 was just read from:
-  // every wave must have finished those reads first.
+  f32x16 s_nxt[NG][kKT];
+  bf16x8 pb[NG][kCH];
+  qk(0, s_nxt);
+  // Slot 0 loads K tile 2 into the buffer tile 0 was just read from: every
+  // wave must have finished those reads first.
   __syncthreads();
-  mask_tail(s_cur, 0);
-  // Reference max from tile 0; s_cur then holds the exponent form
-  // t = s * scale * log2(e) - m_ref.
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    l_run[g] = 0.f;
-    m_ref[g] = max_with_partner32(row_max(s_cur[g])) * c2;
-    const float neg_m = -m_ref[g];
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_cur[g][kt][r] = fmaf(s_cur[g][kt][r], c2, neg_m);
-  }
 
-  auto iteration = [&](auto buf_c, int t) {
-    constexpr int cur = decltype(buf_c)::value;  // = t % 2
-    constexpr int nxt = cur ^ 1;
-    const bool has1 = t + 1 < n_tiles, has2 = t + 2 < n_tiles;
-    if (has2) dma_tile(IsK{}, Kh, k_lds[cur], (t + 2) * kBc);
-    if (has1) dma_tile(IsV{}, Vh, v_lds[nxt], (t + 1) * kBc);
-
-    // ---- matrix cores: S for tile t + 1; vector ALU: weights of tile t ----
-    // (Branch-free so the two interleave.  On the last tile the product reads
-    // an allocated, unused K buffer and its result is dropped.)  K-operand
-    // reads run kKD products ahead of their use: each product's operand read
-    // is issued as a value of its own, and the scheduling groups below fix
-    // the order read, product, vector work.  The two 32-key accumulators
-    // alternate so consecutive products are independent.
-    f32x16 s_nxt[NG][kKT];
-    constexpr int kQK = kKT * G::kChunks;
-    constexpr int kKD = kKDepth;
-    bf16x8 kr[kQK];
-    auto kread = [&](int i) -> bf16x8 {
-      const int c = i / kKT, kt = i % kKT;
-      if (G::kHalfTail && c == G::kChunks - 1 && hi) return bf16x8{};
-      return __builtin_bit_cast(bf16x8, k_lds[nxt][kt * 32 * G::kOct + k_unit[c]]);
-    };
+  // W(t): scores of tile t (raw, in s_nxt) -> weights pb, normaliser share.
+  auto w_phase = [&](int t) __attribute__((always_inline)) {
+    mask_tail(s_nxt, t * kBc);
 #pragma unroll
-    for (int i = 0; i < kKD && i < kQK; ++i) kr[i] = kread(i);
-    __builtin_amdgcn_sched_group_barrier(0x100, kKD, 0);
+    for (int g = 0; g < NG; ++g) {
+      if (t == 0) {  // reference max from tile 0
+        l_run[g] = 0.f;
+        m_ref[g] = max_with_partner32(row_max(s_nxt[g])) * c2;
+      }
+      const float neg_m = -m_ref[g];
 #pragma unroll
-    for (int i = 0; i < kQK; ++i) {
-      if (i + kKD < kQK) kr[i + kKD] = kread(i + kKD);
-      const int c = i / kKT, kt = i % kKT;
+      for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-      for (int g = 0; g < NG; ++g) s_nxt[g][kt] = mfma32(kr[i], qf[g][c], c == 0 ? f32x16{} : s_nxt[g][kt]);
-      if (i + kKD < kQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, kQkValu, 0);  // VALU
+        for (int r = 0; r < 16; ++r) s_nxt[g][kt][r] = fmaf(s_nxt[g][kt][r], c2, neg_m);
     }
-
-    bf16x8 pb[NG][kCH];
     float ls[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -416,7 +397,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       for (int ch = 0; ch < kCH; ++ch)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          pb[g][ch][j] = (__bf16)fast_exp2(s_cur[g][ch >> 1][8 * (ch & 1) + j]);
+          pb[g][ch][j] = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
       // The normaliser sums the same bf16 weights the product uses; this
       // lane's share of it also bounds every weight the lane holds.
       float ls0 = 0.f, ls1 = 0.f;
@@ -429,7 +410,6 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       }
       ls[g] = ls0 + ls1;
     }
-
     // Rare: a lane's share of a row's sum exceeds the limit (so some weight
     // there exceeds 2^9), i.e. the row's scores grew well past its reference
     // max.  Rows whose tile max exceeds the reference by more than kTau move
@@ -441,7 +421,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     if (__builtin_amdgcn_ballot_w64(any_big)) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float mx = max_with_partner32(row_max(s_cur[g]));
+        const float mx = max_with_partner32(row_max(s_nxt[g]));
         const bool grow = mx > kTau;
         const float delta = grow ? mx : 0.f;
         const float alpha = fast_exp2(-delta);
@@ -456,7 +436,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
         for (int ch = 0; ch < kCH; ++ch) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const __bf16 re = (__bf16)fast_exp2(s_cur[g][ch >> 1][8 * (ch & 1) + j] - delta);
+            const __bf16 re = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j] - delta);
             pb[g][ch][j] = grow ? re : pb[g][ch][j];
           }
           ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][0], pb[g][ch][1]}, ones, ls0, false);
@@ -469,28 +449,50 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g) l_run[g] += ls[g];
+  };
 
-    // ---- O^T += V^T P^T (16 keys per product, each V operand read feeding
-    // all NG groups); vector ALU: exponent form of tile t + 1's scores.  Slot
-    // j of half-wave h holds key 8 (j / 4) + 4 h + j % 4 of the chunk on both
-    // operands.  The two transposing reads of a product are issued kVD
-    // products ahead; each product is followed by its share of the
-    // exponent-form arithmetic.
-    const __bf16* vb = reinterpret_cast<const __bf16*>(v_lds[cur]);
+  // M(t) with K(t+1) in buffer kb and V(t) in buffer vb (compile-time).
+  auto m_phase = [&](auto kb_c, auto vb_c, int t) __attribute__((always_inline)) {
+    constexpr int kb = decltype(kb_c)::value, vbi = decltype(vb_c)::value;
+    __builtin_amdgcn_s_setprio(1);
+    if (t + 1 < n_tiles) {
+      // S^T = K Q^T for tile t + 1; K-operand reads kKD products ahead, the
+      // two 32-key accumulators alternate.
+      constexpr int kQK = kKT * G::kChunks;
+      constexpr int kKD = kKDepth;
+      bf16x8 kr[kQK];
+      auto kread = [&](int i) -> bf16x8 {
+        const int c = i / kKT, kt = i % kKT;
+        if (G::kHalfTail && c == G::kChunks - 1 && hi) return bf16x8{};
+        return __builtin_bit_cast(bf16x8, k_lds[kb][kt * 32 * G::kOct + k_unit[c]]);
+      };
+#pragma unroll
+      for (int i = 0; i < kKD && i < kQK; ++i) kr[i] = kread(i);
+      __builtin_amdgcn_sched_group_barrier(0x100, kKD, 0);
+#pragma unroll
+      for (int i = 0; i < kQK; ++i) {
+        if (i + kKD < kQK) kr[i + kKD] = kread(i + kKD);
+        const int c = i / kKT, kt = i % kKT;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) s_nxt[g][kt] = mfma32(kr[i], qf[g][c], c == 0 ? f32x16{} : s_nxt[g][kt]);
+        if (i + kKD < kQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);                    // MFMA
+      }
+    }
+    // O^T += V^T P^T for tile t (16 keys per product).  Slot j of half-wave h
+    // holds key 8 (j / 4) + 4 h + j % 4 of the chunk on both operands; the
+    // two transposing reads of a product are issued kVD products ahead.
+    const __bf16* vbase = reinterpret_cast<const __bf16*>(v_lds[vbi]);
     constexpr int kPV = kCH * G::kDTiles;
     constexpr int kVD = kVDepth;
-    constexpr int kSV = kKT * 16;  // exponent-form values per group
     bf16x8 vr[kPV];
     auto vread = [&](int j) -> bf16x8 {
       const int ch = j / G::kDTiles, dt = j % G::kDTiles;
-      const __bf16* vp = vb + v_off[dt] + 16 * ch * G::kOct * 8;
+      const __bf16* vp = vbase + v_off[dt] + 16 * ch * G::kOct * 8;
       const bf16x4 lo = lds_read_tr16(vp);
       const bf16x4 up = lds_read_tr16(vp + 8 * G::kOct * 8);
       return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
     };
-    float neg_m[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) neg_m[g] = -m_ref[g];
 #pragma unroll
     for (int j = 0; j < kVD && j < kPV; ++j) vr[j] = vread(j);
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVD, 1);
@@ -500,36 +502,53 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       const int ch = j / G::kDTiles, dt = j % G::kDTiles;
 #pragma unroll
       for (int g = 0; g < NG; ++g) acc[g][dt] = mfma32(vr[j], pb[g][ch], acc[g][dt]);
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int e = j * kSV / kPV; e < (j + 1) * kSV / kPV; ++e)
-          s_nxt[g][e / 16][e % 16] = fmaf(s_nxt[g][e / 16][e % 16], c2, neg_m[g]);
       if (j + kVD < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, NG, 1);      // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 2 * NG, 1);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, NG, 1);                    // MFMA
     }
-
-    dma_wait();
-    __syncthreads();
-    // Unconditional (after the last tile the values are simply unused), so
-    // the exponent-form arithmetic above stays interleaved with the PV
-    // products instead of being sunk past the barrier.
-    mask_tail(s_nxt, (t + 1) * kBc);
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) s_cur[g][kt] = s_nxt[g][kt];
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  int t = 0;
-  for (; t + 2 <= n_tiles; t += 2) {
-    iteration(I0{}, t);
-    iteration(I1{}, t + 1);
+  w_phase(0);
+
+  // One slot; p = slot index mod 4 (compile-time), so the buffer of every
+  // tile a slot touches is known: in slots 4j + {0, 1} tile k is even, in
+  // slots 4j + {2, 3} odd (k = slot / 2 rounded down).
+  auto run_slot = [&](auto p_c, int s) __attribute__((always_inline)) {
+    constexpr int p = decltype(p_c)::value;
+    constexpr int kpar = p >> 1;  // parity of k
+    using KP = std::integral_constant<int, kpar>;
+    using KQ = std::integral_constant<int, kpar ^ 1>;
+    const int k = s >> 1;
+    if constexpr ((p & 1) == 0) {
+      if (grp == 1) {  // group B is in its vector phase in even slots
+        if (k + 2 < n_tiles) dma_tile(IsK{}, Kh, k_lds[kpar], (k + 2) * kBc);
+        if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], (k + 1) * kBc);
+      }
+      if (grp == 0) {
+        if (k < n_tiles) m_phase(KQ{}, KP{}, k);
+      } else {
+        if (k >= 1 && k < n_tiles) w_phase(k);
+      }
+    } else {
+      if (grp == 0) {
+        if (k + 1 < n_tiles) w_phase(k + 1);
+      } else {
+        if (k < n_tiles) m_phase(KQ{}, KP{}, k);
+      }
+      dma_wait();
+    }
+    __syncthreads();
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  for (int s = 0; s < 2 * n_tiles; s += 4) {
+    run_slot(P0{}, s);
+    run_slot(P1{}, s + 1);
+    run_slot(P2{}, s + 2);
+    run_slot(P3{}, s + 3);
   }
-  if (t < n_tiles) iteration(I0{}, t);
 
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
