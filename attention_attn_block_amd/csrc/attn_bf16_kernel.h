@@ -228,9 +228,10 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   }
 
   // Tile staging: global -> LDS directly (buffer_load_dwordx4 ... lds, no
-  // registers).  Wave w's j-th load writes LDS units 64 (4j + w) .. +63, lane
-  // i the unit 64 (4j + w) + i; the unit stored there is row p / kOct, stored
-  // column p % kOct, which holds global column (p % kOct) ^ swz(row).
+  // registers), by the four waves of one group (w = wave mod 4).  Wave w's
+  // j-th load writes LDS units 64 (4j + w) .. +63, lane i the unit
+  // 64 (4j + w) + i; the unit stored there is row p / kOct, stored column
+  // p % kOct, which holds global column (p % kOct) ^ swz(row).
   const int wv = __builtin_amdgcn_readfirstlane(wave & 3);
   const int dtid = tid & (kDmaThreads - 1);
   // Byte offsets of this lane's unit inside a full K / V tile (fixed for the
