@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     DitError,
     attn_block_fwd,
     attn_block_fwd_merge,
+    attn_block_workspace,
     attn_lse_merge,
     attn_patch_fwd,
     cfg_combine,

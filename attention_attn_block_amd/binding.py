@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libdit_attn.so")
 DIT_OK, DIT_ERR_INVALID_ARG, DIT_ERR_UNSUPPORTED, DIT_ERR_HIP = 0, 1, 2, 3
 DIT_F32, DIT_BF16 = 0, 1
 
-EXPORTS = ("attn_block_fwd", "attn_block_fwd_merge", "attn_lse_merge", "attn_patch_fwd",
+EXPORTS = ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws",
+           "attn_block_workspace_bytes", "attn_lse_merge", "attn_patch_fwd",
            "cfg_combine", "cfg_combine_relmae", "cfg_combine_relmae_workspace",
            "dit_status_string")
 
@@ -43,14 +44,17 @@ def load():
     vp, i, ll, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float
     L.attn_block_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     L.attn_block_fwd_merge.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    L.attn_block_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, ll, vp]
+    L.attn_block_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_block_workspace_bytes.restype = ll
     L.attn_lse_merge.argtypes = [vp, vp, vp, vp, ll, i, i, vp]
     L.attn_patch_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     L.cfg_combine.argtypes = [vp, vp, vp, ll, f, vp]
     L.cfg_combine_relmae.argtypes = [vp, vp, vp, ll, f, vp, vp, vp]
     L.cfg_combine_relmae_workspace.argtypes = [ll]
     L.cfg_combine_relmae_workspace.restype = ll
-    for name in ("attn_block_fwd", "attn_block_fwd_merge", "attn_lse_merge", "attn_patch_fwd",
-                 "cfg_combine", "cfg_combine_relmae"):
+    for name in ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws", "attn_lse_merge",
+                 "attn_patch_fwd", "cfg_combine", "cfg_combine_relmae"):
         getattr(L, name).restype = ctypes.c_int
     L.dit_status_string.argtypes = [ctypes.c_int]
     L.dit_status_string.restype = ctypes.c_char_p
@@ -96,8 +100,40 @@ def default_scale(d):
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
 
 
-def attn_block_fwd(q, k, v, scale=None, out_dtype=None, out=None, lse=None):
-    """(O, LSE) = attention of q [B,H,Nq,d] against k, v [B,H,Nkv,d]."""
+def attn_block_workspace(q, k):
+    """Zero-filled workspace for the split calls (attn_block_fwd and
+    attn_block_fwd_merge with workspace=) of q against k's shape.  Reusable by
+    later calls of the same or smaller shape, one call at a time."""
+    B, H, Nq, d = q.shape
+    n = load().attn_block_workspace_bytes(B, H, Nq, k.shape[2], d)
+    if n <= 0:
+        raise ValueError("unsupported attention shape")
+    return torch.zeros(n, dtype=torch.uint8, device=q.device)
+
+
+WS_MERGE, WS_FORCE_SPLIT = 1, 2
+
+
+def _attn_ws(fn, q, k, v, o, lse, scale, merge, workspace, force_split=False):
+    dev = _dev(q, k, v, o, lse, workspace)
+    B, H, Nq, d = q.shape
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor (attn_block_workspace)")
+    with torch.cuda.device(dev):
+        rc = load().attn_block_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), B, H, Nq, k.shape[2], d, scale,
+                                      _dtype(q.dtype), _dtype(o.dtype),
+                                      (WS_MERGE if merge else 0) | (WS_FORCE_SPLIT if force_split else 0),
+                                      workspace.data_ptr(), workspace.numel(), _stream(dev))
+    _check(fn, rc)
+
+
+def attn_block_fwd(q, k, v, scale=None, out_dtype=None, out=None, lse=None, workspace=None,
+                   force_split=False):
+    """(O, LSE) = attention of q [B,H,Nq,d] against k, v [B,H,Nkv,d].  With a
+    workspace (attn_block_workspace) the library may share a query tile's
+    keys between workgroups to fill the GPU (attn_block_fwd_ws); force_split
+    takes that path for short blocks too."""
     dev = _dev(q, k, v)
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
@@ -113,6 +149,9 @@ def attn_block_fwd(q, k, v, scale=None, out_dtype=None, out=None, lse=None):
     if out.shape != (B, H, Nq, d) or out.dtype != out_dtype or lse.shape != (B, H, Nq) \
             or lse.dtype != torch.float32:
         raise ValueError("out/lse shape or dtype mismatch")
+    if workspace is not None:
+        _attn_ws("attn_block_fwd_ws", q, k, v, out, lse, scale, False, workspace, force_split)
+        return out, lse
     with torch.cuda.device(dev):
         rc = load().attn_block_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    lse.data_ptr(), B, H, Nq, Nkv, d, scale, _dtype(q.dtype),
@@ -121,9 +160,10 @@ def attn_block_fwd(q, k, v, scale=None, out_dtype=None, out=None, lse=None):
     return out, lse
 
 
-def attn_block_fwd_merge(q, k, v, o_acc, lse_acc, scale=None):
+def attn_block_fwd_merge(q, k, v, o_acc, lse_acc, scale=None, workspace=None, force_split=False):
     """Fold the attention of q against this KV block into (o_acc, lse_acc) in
-    place; rows with lse_acc = -inf are empty and take the block's result."""
+    place; rows with lse_acc = -inf are empty and take the block's result.
+    workspace, force_split: as for attn_block_fwd."""
     dev = _dev(q, k, v, o_acc, lse_acc)
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
@@ -133,6 +173,9 @@ def attn_block_fwd_merge(q, k, v, o_acc, lse_acc, scale=None):
             or lse_acc.dtype != torch.float32:
         raise ValueError("o_acc/lse_acc shape or dtype mismatch")
     scale = default_scale(d) if scale is None else float(scale)
+    if workspace is not None:
+        _attn_ws("attn_block_fwd_ws", q, k, v, o_acc, lse_acc, scale, True, workspace, force_split)
+        return o_acc, lse_acc
     with torch.cuda.device(dev):
         rc = load().attn_block_fwd_merge(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                          o_acc.data_ptr(), lse_acc.data_ptr(), B, H, Nq, Nkv, d,

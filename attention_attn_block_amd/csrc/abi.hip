@@ -64,10 +64,10 @@ bool outputs_clash(const void* O, size_t ob, const float* L, size_t lb, const vo
 
 dit_status_t run_attn(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH,
                       int Nq, int Nkv, int d, float scale, int in_dtype, int out_dtype, bool merge,
-                      hipStream_t stream) {
+                      void* ws, bool force_split, hipStream_t stream) {
   if (in_dtype == DIT_BF16)
     return from_hip(dit::launch_attn_bf16(Q, K, V, O, LSE, BH, Nq, Nkv, d, scale,
-                                          out_dtype == DIT_F32, merge, stream));
+                                          out_dtype == DIT_F32, merge, ws, force_split, stream));
   return from_hip(dit::launch_attn_f32(static_cast<const float*>(Q), static_cast<const float*>(K),
                                        static_cast<const float*>(V), static_cast<float*>(O), LSE,
                                        BH, Nq, Nkv, d, scale, merge, stream));
@@ -87,7 +87,8 @@ dit_status_t attn_block_fwd(const void* Q, const void* K, const void* V, void* O
   const void* ins[3] = {Q, K, V};
   const size_t inb[3] = {qb, kvb, kvb};
   if (outputs_clash(O, ob, LSE, lb, ins, inb, 3)) return DIT_ERR_INVALID_ARG;
-  return run_attn(Q, K, V, O, LSE, B * H, Nq, Nkv, d, scale, in_dtype, out_dtype, false, stream);
+  return run_attn(Q, K, V, O, LSE, B * H, Nq, Nkv, d, scale, in_dtype, out_dtype, false, nullptr,
+                  false, stream);
 }
 
 dit_status_t attn_block_fwd_merge(const void* Q, const void* K, const void* V, void* O_acc,
@@ -102,7 +103,36 @@ dit_status_t attn_block_fwd_merge(const void* Q, const void* K, const void* V, v
   const size_t inb[3] = {qb, kvb, kvb};
   if (outputs_clash(O_acc, ob, LSE_acc, lb, ins, inb, 3)) return DIT_ERR_INVALID_ARG;
   return run_attn(Q, K, V, O_acc, LSE_acc, B * H, Nq, Nkv, d, scale, in_dtype, acc_dtype, true,
-                  stream);
+                  nullptr, false, stream);
+}
+
+long long attn_block_workspace_bytes(int B, int H, int Nq, int Nkv, int d) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nkv <= 0 || !head_dim_ok(d)) return 0;
+  const long long items = (long long)B * H * ((Nq + dit::kAttnRowsPerTile - 1) / dit::kAttnRowsPerTile);
+  return dit::attn_split_layout(items, d).bytes;
+}
+
+dit_status_t attn_block_fwd_ws(const void* Q, const void* K, const void* V, void* O_acc,
+                               float* LSE_acc, int B, int H, int Nq, int Nkv, int d, float scale,
+                               dit_dtype_t in_dtype, dit_dtype_t out_dtype, int flags,
+                               void* workspace, long long workspace_bytes, hipStream_t stream) {
+  size_t qb, kvb, ob, lb;
+  const dit_status_t st = check_attn(Q, K, V, O_acc, LSE_acc, B, H, Nq, Nkv, d, scale,
+                                     (int)in_dtype, (int)out_dtype, &qb, &kvb, &ob, &lb);
+  if (st != DIT_OK) return st;
+  if (flags & ~(DIT_WS_MERGE | DIT_WS_FORCE_SPLIT)) return DIT_ERR_INVALID_ARG;
+  const long long need = attn_block_workspace_bytes(B, H, Nq, Nkv, d);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return DIT_ERR_INVALID_ARG;
+  const void* ins[3] = {Q, K, V};
+  const size_t inb[3] = {qb, kvb, kvb};
+  if (outputs_clash(O_acc, ob, LSE_acc, lb, ins, inb, 3)) return DIT_ERR_INVALID_ARG;
+  const void* all[5] = {Q, K, V, O_acc, LSE_acc};
+  const size_t allb[5] = {qb, kvb, kvb, ob, lb};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(workspace, (size_t)need, all[i], allb[i])) return DIT_ERR_INVALID_ARG;
+  return run_attn(Q, K, V, O_acc, LSE_acc, B * H, Nq, Nkv, d, scale, in_dtype, out_dtype,
+                  (flags & DIT_WS_MERGE) != 0, workspace, (flags & DIT_WS_FORCE_SPLIT) != 0, stream);
 }
 
 dit_status_t attn_lse_merge(void* O_a, float* LSE_a, const void* O_b, const float* LSE_b,
@@ -151,7 +181,7 @@ dit_status_t attn_patch_fwd(const void* Q_p, const void* K_p, const void* V_p, v
                                      (long long)N * row_units, (long long)p0 * row_units, stream);
   if (e != hipSuccess) return DIT_ERR_HIP;
   return run_attn(Q_p, K_buf, V_buf, O, LSE, B * H, Np, N, d, scale, in_dtype, out_dtype, false,
-                  stream);
+                  nullptr, false, stream);
 }
 
 dit_status_t cfg_combine(const float* eps_u, const float* eps_c, float* out, long long n, float s,

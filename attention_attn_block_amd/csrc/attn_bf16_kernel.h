@@ -67,6 +67,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 512;   // 8 waves: two per SIMD, ping-pong
 constexpr int kDmaThreads = 256;  // the tile loads are issued by one group of 4 waves
 constexpr int kBc = 64;         // keys per KV tile (a multiple of 32)
+constexpr int kMaxPieces = kAttnMaxPieces;  // SPLIT: workgroups per query tile, at most
 constexpr int kKT = kBc / 32;   // 32-key score accumulators per tile
 constexpr int kCH = kBc / 16;   // 16-key chunks of the PV product per tile
 constexpr int kWavesPerSimd = 2;  // with one query group per wave
@@ -175,10 +176,18 @@ __device__ __forceinline__ float row_max(const f32x16* s) {
 // matrix work, but it needs one wave per SIMD and about 512 registers, and the
 // compiler then spills heavily; kGroups is 1 (the ping-pong schedule also
 // assumes one group).
-template <int D, int NG, bool OUT_F32, bool MERGE>
+//
+// SPLIT: the grid is a fixed number of workgroups that share the
+// (query tile, key tile) work evenly, so a query tile's key range may be cut
+// between up to kMaxPieces workgroups (the launcher checks).  Each piece ends
+// with its own partial (O, LSE); the partials of a tile are combined with the
+// log-sum-exp identity by whichever piece arrives last, through the caller's
+// workspace.
+template <int D, int NG, bool OUT_F32, bool MERGE, bool SPLIT>
 __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    void* __restrict__ Out, float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, float c2) {
+    void* __restrict__ Out, float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, float c2,
+    int n_items, unsigned* __restrict__ ws_count, float* __restrict__ ws_part) {
   using G = Geo<D>;
   constexpr int kRowsWG = (kThreads / 64) * 32 * NG;  // query rows per workgroup
   // K and V tiles: kBc rows of kOct 16-byte units each, unit-swizzled (see
@@ -187,6 +196,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   constexpr int kBufUnits = kTileUnits + 16;
   __shared__ u32x4 k_lds[2][kBufUnits];
   __shared__ u32x4 v_lds[2][kBufUnits];
+  __shared__ unsigned s_arrive;  // SPLIT: counter value seen by this workgroup
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -202,31 +212,19 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   const int slot = bid >> 3;
   const int per = nblk >> 3, rem = nblk & 7;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int bh = logical / n_qtiles;
-  const int qt = logical - bh * n_qtiles;
+  const int n_all = (Nkv + kBc - 1) / kBc;  // key tiles of the block
 
-  const __bf16* Qh = Q + (size_t)bh * Nq * D;
-  const __bf16* Kh = K + (size_t)bh * Nkv * D;
-  const __bf16* Vh = V + (size_t)bh * Nkv * D;
-
-  // Query rows of this lane, one per group; Q^T as the B operand: lane holds
-  // Q[row][16c + 8hi .. +7].
-  int my_q[NG];
-  bf16x8 qf[NG][G::kChunks];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    my_q[g] = qt * kRowsWG + (wave * NG + g) * 32 + l32;
-    const int q_ld = my_q[g] < Nq ? my_q[g] : Nq - 1;
-#pragma unroll
-    for (int c = 0; c < G::kChunks; ++c) {
-      if (G::kHalfTail && c == G::kChunks - 1 && hi) {
-        qf[g][c] = bf16x8{};
-      } else {
-        qf[g][c] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)q_ld * D + 16 * c + 8 * hi);
-      }
-    }
+  // Work units are (query tile, key tile) pairs in query-tile-major order;
+  // this workgroup owns units [u, u_end).  Unsplit: exactly one query tile.
+  long long u, u_end;
+  if constexpr (SPLIT) {
+    const long long total = (long long)n_items * n_all;
+    u = total * logical / nblk;
+    u_end = total * (logical + 1) / nblk;
+  } else {
+    u = (long long)logical * n_all;
+    u_end = u + n_all;
   }
-
   // Tile staging: global -> LDS directly (buffer_load_dwordx4 ... lds, no
   // registers), by the four waves of one group (w = wave mod 4).  Wave w's
   // j-th load writes LDS units 64 (4j + w) .. +63, lane i the unit
@@ -287,6 +285,38 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 #pragma unroll
   for (int c = 0; c < G::kChunks; ++c) k_unit[c] = l32 * G::kOct + (((2 * c + hi) ^ sk) % G::kOct);
 
+  while (u < u_end) {
+  // One piece: key tiles [t_beg, t_end) of query tile `item`.
+  const int item = (int)(u / n_all);
+  const int t_beg = (int)(u - (long long)item * n_all);
+  const int t_end = (int)(u_end - u < (long long)(n_all - t_beg) ? t_beg + (u_end - u) : n_all);
+  u += t_end - t_beg;
+  const int bh = item / n_qtiles;
+  const int qt = item - bh * n_qtiles;
+  const int kvb = t_beg * kBc;  // first key of the piece
+
+  const __bf16* Qh = Q + (size_t)bh * Nq * D;
+  const __bf16* Kh = K + (size_t)bh * Nkv * D;
+  const __bf16* Vh = V + (size_t)bh * Nkv * D;
+
+  // Query rows of this lane, one per group; Q^T as the B operand: lane holds
+  // Q[row][16c + 8hi .. +7].
+  int my_q[NG];
+  bf16x8 qf[NG][G::kChunks];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    my_q[g] = qt * kRowsWG + (wave * NG + g) * 32 + l32;
+    const int q_ld = my_q[g] < Nq ? my_q[g] : Nq - 1;
+#pragma unroll
+    for (int c = 0; c < G::kChunks; ++c) {
+      if (G::kHalfTail && c == G::kChunks - 1 && hi) {
+        qf[g][c] = bf16x8{};
+      } else {
+        qf[g][c] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)q_ld * D + 16 * c + 8 * hi);
+      }
+    }
+  }
+
   // S^T = K Q^T for the kBc keys of the K tile in LDS buffer `buf`; each K
   // operand read feeds the products of all NG query groups.
   auto qk = [&](int buf, f32x16 (*s)[kKT]) {
@@ -346,7 +376,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   float l_run[NG];   // this lane's share of each row's normaliser (bf16 weights)
   float m_ref[NG];   // reference row max for the exponentials, log2 units
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-  const int n_tiles = (Nkv + kBc - 1) / kBc;
+  const int n_tiles = t_end - t_beg;  // key tiles of this piece
 
   // Ping-pong schedule.  Waves w and w + 4 share a SIMD.  Group A (waves 0-3)
   // and group B (waves 4-7) run the same per-wave pipeline one slot apart, so
@@ -362,9 +392,9 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // slot 2k+1 ends by waiting for them.
   const int grp = wave >> 2;
   if (grp == 1) {
-    dma_tile(IsK{}, Kh, k_lds[0], 0);
-    dma_tile(IsV{}, Vh, v_lds[0], 0);
-    if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kBc);
+    dma_tile(IsK{}, Kh, k_lds[0], kvb);
+    dma_tile(IsV{}, Vh, v_lds[0], kvb);
+    if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kvb + kBc);
   }
   dma_wait();
   __syncthreads();
@@ -378,7 +408,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 
   // W(t): scores of tile t (raw, in s_nxt) -> weights pb, normaliser share.
   auto w_phase = [&](int t) __attribute__((always_inline)) {
-    mask_tail(s_nxt, t * kBc);
+    mask_tail(s_nxt, kvb + t * kBc);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (t == 0) {  // reference max from tile 0
@@ -522,8 +552,8 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     const int k = s >> 1;
     if constexpr ((p & 1) == 0) {
       if (grp == 1) {  // group B is in its vector phase in even slots
-        if (k + 2 < n_tiles) dma_tile(IsK{}, Kh, k_lds[kpar], (k + 2) * kBc);
-        if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], (k + 1) * kBc);
+        if (k + 2 < n_tiles) dma_tile(IsK{}, Kh, k_lds[kpar], kvb + (k + 2) * kBc);
+        if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], kvb + (k + 1) * kBc);
       }
       if (grp == 0) {
         if (k < n_tiles) m_phase(KQ{}, KP{}, k);
@@ -551,91 +581,317 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     run_slot(P3{}, s + 3);
   }
 
+  if (!SPLIT || (t_beg == 0 && t_end == n_all)) {
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const float l_tot = sum_with_partner32(l_run[g]);
-    if (my_q[g] < Nq) {
-      // This block's partial: O_b = acc / l_tot, LSE_b = m_ref + log2 l_tot
-      // (log2 units).  MERGE folds it into the running (Out, LSE) of the row
-      // with the log-sum-exp identity; LSE = -inf there marks an empty
-      // accumulator whose O is not read.
-      const size_t lrow = (size_t)bh * Nq + my_q[g];
-      const float lse_b = m_ref[g] + fast_log2(l_tot);
-      float wb = 1.f / l_tot, wa = 0.f, lse_new = lse_b;
-      bool has_a = false;
-      if constexpr (MERGE) {
-        const float la = LSE[lrow] * kLog2e;
-        has_a = la != -INFINITY;
-        if (has_a) {
-          const float m = fmaxf(la, lse_b);
-          const float ea = fast_exp2(la - m), eb = fast_exp2(lse_b - m);
-          const float inv = 1.f / (ea + eb);
-          wa = ea * inv;
-          wb = eb * inv / l_tot;
-          lse_new = m + fast_log2(ea + eb);
+    for (int g = 0; g < NG; ++g) {
+      const float l_tot = sum_with_partner32(l_run[g]);
+      if (my_q[g] < Nq) {
+        // This block's partial: O_b = acc / l_tot, LSE_b = m_ref + log2 l_tot
+        // (log2 units).  MERGE folds it into the running (Out, LSE) of the row
+        // with the log-sum-exp identity; LSE = -inf there marks an empty
+        // accumulator whose O is not read.
+        const size_t lrow = (size_t)bh * Nq + my_q[g];
+        const float lse_b = m_ref[g] + fast_log2(l_tot);
+        float wb = 1.f / l_tot, wa = 0.f, lse_new = lse_b;
+        bool has_a = false;
+        if constexpr (MERGE) {
+          const float la = LSE[lrow] * kLog2e;
+          has_a = la != -INFINITY;
+          if (has_a) {
+            const float m = fmaxf(la, lse_b);
+            const float ea = fast_exp2(la - m), eb = fast_exp2(lse_b - m);
+            const float inv = 1.f / (ea + eb);
+            wa = ea * inv;
+            wb = eb * inv / l_tot;
+            lse_new = m + fast_log2(ea + eb);
+          }
         }
+        const size_t orow = lrow * D;
+#pragma unroll
+        for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+            if (d0 < D) {
+              float o[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = acc[g][dt][4 * q4 + e] * wb;
+              if constexpr (OUT_F32) {
+                f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
+                if (MERGE && has_a) {
+                  const f32x4 a = *p;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], o[e]);
+                }
+                *p = f32x4{o[0], o[1], o[2], o[3]};
+              } else {
+                bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
+                if (MERGE && has_a) {
+                  const bf16x4 a = *p;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], o[e]);
+                }
+                *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+              }
+            }
+          }
+        if (hi == 0) LSE[lrow] = lse_new * kLn2;
       }
-      const size_t orow = lrow * D;
+    }
+  } else {
+    // One of the k (2..kMaxPieces) pieces of a query tile whose key range
+    // is cut between workgroups; piece j holds the j-th key range.  All
+    // partials take one representation -- O normalised, in fp32, and LSE in
+    // log2 units -- and are combined in key order, so the result is the same
+    // bits whichever piece combines.
+    constexpr int kSlot = kRowsWG * (D + 1);  // floats per partial: O rows, then LSE
+    const long long total = (long long)n_items * n_all;
+    // Workgroup whose range holds unit x (ranges start at total * w / nblk).
+    auto owner = [&](long long x) { return ((x + 1) * nblk + total - 1) / total - 1; };
+    const long long w_first = owner((long long)item * n_all);
+    const int n_pieces = (int)(owner((long long)item * n_all + n_all - 1) - w_first + 1);
+    const int j_piece = (int)(logical - w_first);
+    float* slots = ws_part + (size_t)item * kMaxPieces * kSlot;
+    float lse_own[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const float l_tot = sum_with_partner32(l_run[g]);
+      lse_own[g] = m_ref[g] + fast_log2(l_tot);
+      const float inv = 1.f / l_tot;
 #pragma unroll
       for (int dt = 0; dt < G::kDTiles; ++dt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = dt * 32 + 8 * q4 + 4 * hi;
-          if (d0 < D) {
-            float o[4];
+        for (int r = 0; r < 16; ++r) acc[g][dt][r] *= inv;
+    }
+    // Partials are written and read with device-coherent buffer accesses
+    // (sc1, the encoding of device-scope atomic loads and stores: coherent
+    // across the per-XCD L2s), so the exchange needs no L2 write-back or
+    // invalidate -- those would also drop the K/V tiles other workgroups are
+    // reusing from L2.
+    auto slot_rsrc = [&](int j) {
+      return __builtin_amdgcn_make_buffer_rsrc(slots + (size_t)j * kSlot, (short)0, kSlot * 4,
+                                               kBufferFlags);
+    };
+    constexpr int kCoherent = 16;  // sc1
+    auto publish = [&]() {
+      const __amdgpu_buffer_rsrc_t own = slot_rsrc(j_piece);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = acc[g][dt][4 * q4 + e] * wb;
-            if constexpr (OUT_F32) {
-              f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
-              if (MERGE && has_a) {
-                const f32x4 a = *p;
+      for (int g = 0; g < NG; ++g) {
+        if (my_q[g] >= Nq) continue;
+        const int row = (wave * NG + g) * 32 + l32;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], o[e]);
+        for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+            if (d0 < D)
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  __builtin_bit_cast(u32x4, f32x4{acc[g][dt][4 * q4], acc[g][dt][4 * q4 + 1],
+                                                  acc[g][dt][4 * q4 + 2], acc[g][dt][4 * q4 + 3]}),
+                  own, (row * D + d0) * 4, 0, kCoherent);
+          }
+        if (hi == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_own[g]), own,
+                                                (kRowsWG * D + row) * 4, 0, kCoherent);
+      }
+    };
+    // Arrival on the tile's counter (0 before the first piece arrives; the
+    // combining piece sets it back to 0).  The low 16 bits count arrivals,
+    // bit 16 says piece 0 has published.
+    //   piece j > 0: publish, add 1; combine iff the counter was
+    //                2^16 + (k - 1) (piece 0 published, every other piece in).
+    //   piece 0:     add 1; combine iff it was k - 1 (every other piece has
+    //                published).  Otherwise publish, add 2^16, and combine iff
+    //                the arrivals then numbered k.
+    // Piece 0 ends its workgroup's range and usually arrives last, so it
+    // usually combines without publishing.  Exactly one piece combines, only
+    // after every other partial is published, and no workgroup ever waits
+    // for another.  The counter is a relaxed device-scope atomic; each
+    // arrival first waits until this workgroup's coherent stores are
+    // acknowledged.
+    unsigned* cnt = ws_count + item;
+    auto arrive = [&](unsigned add) -> unsigned {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own published stores acknowledged
+      __syncthreads();
+      if (tid == 0)
+        s_arrive = __hip_atomic_fetch_add(cnt, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      return s_arrive;
+    };
+    constexpr unsigned kPublished0 = 1u << 16;
+    const unsigned others = (unsigned)n_pieces - 1u;
+    bool combine;
+    if (j_piece > 0) {
+      publish();
+      combine = arrive(1u) == kPublished0 + others;
+    } else {
+      const unsigned first = arrive(1u);
+      if (first == others) {
+        combine = true;
+      } else {
+        publish();
+        combine = (arrive(kPublished0) & 0xffffu) == others + 1u;
+      }
+    }
+    if (combine) {
+      if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (my_q[g] >= Nq) continue;
+        const int row = (wave * NG + g) * 32 + l32;
+        const size_t lrow = (size_t)bh * Nq + my_q[g];
+        // Weights of the pieces: e_j = 2^(L_j - m), normalised by their sum.
+        // Every slot of the tile is read (all are inside the workspace) and
+        // the ones that are not another piece's published partial are
+        // replaced by selects, so the loads issue back to back without
+        // branches between them.
+        float lp[kMaxPieces], wp[kMaxPieces];
+#pragma unroll
+        for (int j = 0; j < kMaxPieces; ++j)
+          lp[j] = j < n_pieces ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                     slot_rsrc(j), (kRowsWG * D + row) * 4, 0, kCoherent))
+                               : 0.f;
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kMaxPieces; ++j) {
+          lp[j] = j == j_piece ? lse_own[g] : (j < n_pieces ? lp[j] : -INFINITY);
+          m = fmaxf(m, lp[j]);
+        }
+        float esum = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxPieces; ++j) {
+          wp[j] = j < n_pieces ? fast_exp2(lp[j] - m) : 0.f;
+          esum += wp[j];
+        }
+        const float einv = 1.f / esum;
+#pragma unroll
+        for (int j = 0; j < kMaxPieces; ++j) wp[j] *= einv;
+        const float lse_b = m + fast_log2(esum);
+        // Fold into the running (Out, LSE) as in the unsplit epilogue.
+        float wa = 0.f, wb = 1.f, lse_new = lse_b;
+        bool has_a = false;
+        if constexpr (MERGE) {
+          const float la = LSE[lrow] * kLog2e;
+          has_a = la != -INFINITY;
+          if (has_a) {
+            const float m2 = fmaxf(la, lse_b);
+            const float ea = fast_exp2(la - m2), eb = fast_exp2(lse_b - m2);
+            const float inv2 = 1.f / (ea + eb);
+            wa = ea * inv2;
+            wb = eb * inv2;
+            lse_new = m2 + fast_log2(ea + eb);
+          }
+        }
+        const size_t orow = lrow * D;
+#pragma unroll
+        for (int dt = 0; dt < G::kDTiles; ++dt) {
+          // One 32-column tile of each other slot (slot i, or i + 1 from this
+          // piece's own on), loaded back to back.
+          f32x4 pv[kMaxPieces - 1][4];
+#pragma unroll
+          for (int i = 0; i < kMaxPieces - 1; ++i) {
+            if (i < n_pieces - 1) {  // workgroup-uniform
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+                pv[i][q4] = d0 < D ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                   slot_rsrc(i + (i >= j_piece)), (row * D + d0) * 4, 0, kCoherent))
+                                   : f32x4{};
               }
-              *p = f32x4{o[0], o[1], o[2], o[3]};
             } else {
-              bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
-              if (MERGE && has_a) {
-                const bf16x4 a = *p;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], o[e]);
+              for (int q4 = 0; q4 < 4; ++q4) pv[i][q4] = f32x4{};
+            }
+          }
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+            if (d0 < D) {
+              float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int j = 0; j < kMaxPieces; ++j) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  // piece j: own below, else slot j (j < own) or loaded entry j - 1
+                  const float lo = j < kMaxPieces - 1 ? pv[j < kMaxPieces - 1 ? j : 0][q4][e] : 0.f;
+                  const float up = j > 0 ? pv[j > 0 ? j - 1 : 0][q4][e] : 0.f;
+                  const float pj = j == j_piece ? acc[g][dt][4 * q4 + e]
+                                                : (j >= n_pieces ? 0.f : (j < j_piece ? lo : up));
+                  o[e] = fmaf(wp[j], pj, o[e]);
+                }
               }
-              *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+              if constexpr (OUT_F32) {
+                f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
+                if (MERGE && has_a) {
+                  const f32x4 a = *p;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], wb * o[e]);
+                }
+                *p = f32x4{o[0], o[1], o[2], o[3]};
+              } else {
+                bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
+                if (MERGE && has_a) {
+                  const bf16x4 a = *p;
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], wb * o[e]);
+                }
+                *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+              }
             }
           }
         }
-      if (hi == 0) LSE[lrow] = lse_new * kLn2;
+        if (hi == 0) LSE[lrow] = lse_new * kLn2;
+      }
     }
   }
+  if constexpr (SPLIT) __syncthreads();  // LDS is reused by the next piece
+  }  // piece loop
 }
 
 }  // namespace
 
 // Launch for one head dim (explicitly instantiated in the attn_bf16_d*.hip
-// files so the instantiations compile in parallel).
+// files so the instantiations compile in parallel).  split_grid > 0 selects
+// the SPLIT kernel on that many workgroups, with `ws` laid out as
+// attn_split_layout describes.
 template <int D>
 hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH,
-                         int Nq, int Nkv, float scale, bool out_f32, bool merge,
-                         hipStream_t stream) {
+                         int Nq, int Nkv, float scale, bool out_f32, bool merge, int split_grid,
+                         void* ws, hipStream_t stream) {
   constexpr int NG = kGroups;
   constexpr int kRowsWG = (kThreads / 64) * 32 * NG;
+  static_assert(kRowsWG == kAttnRowsPerTile && kBc == kAttnKeysPerTile,
+                "the split planner's tile sizes must match the kernel's");
   const int n_qtiles = (Nq + kRowsWG - 1) / kRowsWG;
-  const dim3 grid((unsigned)(n_qtiles * BH));
+  const int n_items = n_qtiles * BH;
   const float c2 = scale * kLog2e;
   const __bf16* q = static_cast<const __bf16*>(Q);
   const __bf16* k = static_cast<const __bf16*>(K);
   const __bf16* v = static_cast<const __bf16*>(V);
+  using Kern = void (*)(const __bf16*, const __bf16*, const __bf16*, void*, float*, int, int, int,
+                        float, int, unsigned*, float*);
+  const bool split = split_grid > 0;
+  Kern kern;
   if (out_f32) {
     if (merge)
-      attn_fwd_bf16_kernel<D, NG, true, true><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+      kern = split ? attn_fwd_bf16_kernel<D, NG, true, true, true> : attn_fwd_bf16_kernel<D, NG, true, true, false>;
     else
-      attn_fwd_bf16_kernel<D, NG, true, false><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+      kern = split ? attn_fwd_bf16_kernel<D, NG, true, false, true> : attn_fwd_bf16_kernel<D, NG, true, false, false>;
   } else {
     if (merge)
-      attn_fwd_bf16_kernel<D, NG, false, true><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+      kern = split ? attn_fwd_bf16_kernel<D, NG, false, true, true> : attn_fwd_bf16_kernel<D, NG, false, true, false>;
     else
-      attn_fwd_bf16_kernel<D, NG, false, false><<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2);
+      kern = split ? attn_fwd_bf16_kernel<D, NG, false, false, true> : attn_fwd_bf16_kernel<D, NG, false, false, false>;
   }
+  unsigned* ws_count = nullptr;
+  float* ws_part = nullptr;
+  if (split) {
+    const AttnSplitLayout lay = attn_split_layout(n_items, D);
+    ws_count = static_cast<unsigned*>(ws);
+    ws_part = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.part_offset);
+  }
+  const dim3 grid((unsigned)(split ? split_grid : n_items));
+  kern<<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2, n_items, ws_count, ws_part);
   return hipGetLastError();
 }
 

@@ -254,10 +254,11 @@ def main():
 
 def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):
     """Reported beside the step: merge and CFG on cold HBM (rotating buffers
-    larger than the 256 MB Infinity Cache), the fused ring step, and the d=72
+    larger than the 256 MB Infinity Cache), the fused ring step, a long block
+    with few query tiles (plain grid vs split launch), and the d=72
     workloads."""
-    from attention_attn_block_amd import (attn_block_fwd, attn_block_fwd_merge, attn_lse_merge,
-                                          cfg_combine, cfg_combine_relmae)
+    from attention_attn_block_amd import (attn_block_fwd, attn_block_fwd_merge, attn_block_workspace,
+                                          attn_lse_merge, cfg_combine, cfg_combine_relmae)
     res = {}
 
     def timed(fn, iters):
@@ -313,6 +314,29 @@ def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):
     f = len(ks) * attn_flops(B, H, Nq, ks[0].shape[2], dd)
     res["ring_share_fused_merge"] = {"us_per_share": us, "tflops": f / (us * 1e-6) / 1e12,
                                      "frac_bf16_peak": f / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+
+    # Few query tiles against a long block: 20 heads x 2048 queries (160 tiles
+    # of 256 rows on 256 CUs) x 16384 keys, plain grid vs the split launch
+    # (attn_block_fwd_ws), which shares the tiles' keys over every CU.
+    g = torch.Generator(device=dev).manual_seed(7)
+    shp = (1, 20, 2048, 16384, 128)
+    q = torch.randn(shp[0], shp[1], shp[2], shp[4], device=dev, generator=g).to(torch.bfloat16)
+    k = torch.randn(shp[0], shp[1], shp[3], shp[4], device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn(shp[0], shp[1], shp[3], shp[4], device=dev, generator=g).to(torch.bfloat16)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    wsp = attn_block_workspace(q, k)
+    f = attn_flops(shp[0], shp[1], shp[2], shp[3], shp[4])
+    row = {"shape_b_h_nq_nkv_d": list(shp)}
+    for tag, kw in (("plain", {}), ("split", {"workspace": wsp})):
+        fn = lambda i: attn_block_fwd(q, k, v, out=out, lse=lse, out_dtype=torch.float32, **kw)
+        for i in range(10):
+            fn(i)
+        us = timed(fn, 20)
+        row[f"{tag}_us"] = us
+        row[f"{tag}_tflops"] = f / (us * 1e-6) / 1e12
+    res["long_block_160_tiles"] = row
+    del q, k, v, out, lse, wsp
 
     # d = 72 attention: PixArt-style 1024 px and DiT-XL/2 256 px.
     for name in ("pixart_1024", "dit_xl_256"):

@@ -107,6 +107,46 @@ dit_status_t attn_block_fwd_merge(const void* Q, const void* K, const void* V,
                                   dit_dtype_t in_dtype, dit_dtype_t acc_dtype,
                                   hipStream_t stream);
 
+/* Flags of attn_block_fwd_ws. */
+enum {
+  DIT_WS_MERGE = 1,       /* fold into (O_acc, LSE_acc) as attn_block_fwd_merge */
+  DIT_WS_FORCE_SPLIT = 2  /* split whenever the grid allows, whatever the block length */
+};
+
+/*
+ * attn_block_fwd (flags without DIT_WS_MERGE) or attn_block_fwd_merge (with
+ * it) with a workspace that lets the library share one query tile's keys
+ * between up to four workgroups.  A block with few query tiles of 256 rows
+ * (for example 24 heads x 2048 queries: 192 tiles on 256 compute units)
+ * leaves part of the GPU idle when each tile is one workgroup; the workspace
+ * call instead gives every compute unit an equal share of (query tile,
+ * 64-key tile) work, and the partials of a cut tile are combined with the
+ * log-sum-exp identity of attn_lse_merge (SwiftFusion, sections 1-2: blocks
+ * over disjoint keys combine in any grouping).  Which piece combines depends
+ * on timing, but the combination takes a fixed order, so repeated calls give
+ * identical bits.  Results agree with the plain calls to within rounding
+ * (not bit for bit).  The split is taken for blocks of at least 6144 keys
+ * (shorter blocks gain less from the fuller grid than the exchange of
+ * partials costs) unless DIT_WS_FORCE_SPLIT is set; shapes the plain grid
+ * already fills, and fp32 inputs, always run the plain path.
+ *   Q, K, V, O_acc, LSE_acc, dtypes: as attn_block_fwd / attn_block_fwd_merge
+ *   workspace: device memory of at least attn_block_workspace_bytes(...)
+ *              bytes, 256-byte aligned, owned by the caller, overlapping no
+ *              tensor.  It must be zero-filled before its first use; every
+ *              call leaves its arrival counters at zero again.  One workspace
+ *              serves one call at a time (calls that share a workspace on
+ *              different streams race).
+ * Returns DIT_ERR_INVALID_ARG for a null, short, misaligned or overlapping
+ * workspace or unknown flags, otherwise as attn_block_fwd.
+ */
+long long attn_block_workspace_bytes(int B, int H, int Nq, int Nkv, int d);
+dit_status_t attn_block_fwd_ws(const void* Q, const void* K, const void* V,
+                               void* O_acc, float* LSE_acc,
+                               int B, int H, int Nq, int Nkv, int d, float scale,
+                               dit_dtype_t in_dtype, dit_dtype_t out_dtype, int flags,
+                               void* workspace, long long workspace_bytes,
+                               hipStream_t stream);
+
 /*
  * Log-sum-exp merge of two partials over disjoint key sets, in place into a.
  *

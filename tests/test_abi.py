@@ -190,6 +190,54 @@ def test_attn_block_fwd_merge_rejects(lib, kw, code):
 
 
 # ---------------------------------------------------------------------------
+# attn_block_fwd_ws (split launch with a caller workspace)
+# ---------------------------------------------------------------------------
+
+def split_ws_bytes(B, H, Nq, d):
+    """Counters (uint32 per 256-row query tile, padded to 256 B), then four fp32
+    partials (256 rows x (d + 1) floats) per query tile."""
+    items = B * H * ((Nq + 255) // 256)
+    return (items * 4 + 255) // 256 * 256 + items * 4 * 256 * (d + 1) * 4
+
+
+@pytest.mark.parametrize("shape", [(1, 24, 2048, 2048, 128), (2, 16, 4096, 4096, 72),
+                                   (1, 1, 1, 1, 8), (3, 5, 257, 9, 64)])
+def test_block_workspace_bytes(lib, shape):
+    B, H, Nq, Nkv, d = shape
+    assert lib.attn_block_workspace_bytes(B, H, Nq, Nkv, d) == split_ws_bytes(B, H, Nq, d)
+
+
+def test_block_workspace_bytes_invalid(lib):
+    for args in [(0, 1, 1, 1, 64), (1, 0, 1, 1, 64), (1, 1, 0, 1, 64), (1, 1, 1, 0, 64),
+                 (1, 1, 1, 1, 60), (1, 1, 1, 1, 136)]:
+        assert lib.attn_block_workspace_bytes(*args) == 0
+
+
+def block_ws(lib, **kw):
+    a = dict(Q=ptr(0), K=ptr(1), V=ptr(2), O=ptr(3), LSE=ptr(4), B=1, H=24, Nq=2048, Nkv=2048,
+             d=128, scale=0.088, i=BF16, o=F32, flags=0, W=ptr(5), nbytes=None)
+    a.update(kw)
+    n = split_ws_bytes(a["B"], a["H"], a["Nq"], a["d"]) if a["nbytes"] is None else a["nbytes"]
+    return lib.attn_block_fwd_ws(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["H"], a["Nq"],
+                                 a["Nkv"], a["d"], a["scale"], a["i"], a["o"], a["flags"], a["W"],
+                                 n, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), INV),
+    (dict(nbytes=split_ws_bytes(1, 24, 2048, 128) - 1), INV),   # short
+    (dict(W=ptr(5, 16)), INV),                                   # not 256-byte aligned
+    (dict(flags=4), INV), (dict(flags=-1), INV), (dict(flags=8), INV),     # unknown flags
+    (dict(W=ptr(4, 256)), INV),                                  # overlaps LSE
+    (dict(W=ptr(0, 1 << 20)), INV),                              # inside Q
+    (dict(Q=None), INV), (dict(d=60), UNS), (dict(scale=0.0), INV),
+    (dict(O=ptr(2, 32)), INV),                                   # output overlaps V
+])
+def test_attn_block_fwd_ws_rejects(lib, kw, code):
+    assert block_ws(lib, **kw) == code
+
+
+# ---------------------------------------------------------------------------
 # cfg_combine_relmae
 # ---------------------------------------------------------------------------
 

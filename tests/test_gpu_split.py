@@ -1,0 +1,164 @@
+"""GPU parity of the split launch (attn_block_fwd_ws): a query tile's keys
+shared between up to four workgroups, the partials combined through the
+caller's workspace.  Against the fp64 oracle; repeated calls must give
+identical bits and leave the workspace counters at zero.  The short blocks
+force the split (the library takes it on its own only from 6144 keys), so the
+oracle can check every output; one long block runs the default choice and is
+checked on sampled rows."""
+
+import numpy as np
+
+import pytest
+import torch
+
+import oracle
+from attention_attn_block_amd import (attn_block_fwd, attn_block_fwd_merge, attn_block_workspace,
+                                      inputs)
+from attention_attn_block_amd.binding import load
+from tests.gpu_util import assert_bf16_close, to_f64, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(t):
+    return t.to("cuda:0")
+
+
+def counters_zero(ws, B, H, Nq):
+    items = B * H * ((Nq + 255) // 256)
+    return int(ws[: items * 4].view(torch.int32).abs().sum().item()) == 0
+
+
+# Shapes whose plain grid (one 256-row query tile per workgroup) leaves part of
+# a 256-CU GPU idle, so a forced split is taken; the last three are ragged in
+# query rows, keys or both, and cut some query tiles into three pieces.
+SPLIT_SHAPES = [(1, 24, 2048, 2048, 128), (1, 24, 2000, 700, 128), (3, 10, 1111, 517, 72),
+                (1, 150, 256, 333, 64)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_split_block_matches_oracle(shape, out_dtype):
+    B, H, Nq, Nkv, d = shape
+    q, k, v = inputs.attn_inputs(B, H, Nq, Nkv, d, "bf16", seed=Nq + 7 * Nkv + d)
+    scale = inputs.default_scale(d)
+    say("case split block", shape, out_dtype)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    ws = attn_block_workspace(qd, kd)
+    O, L = attn_block_fwd(qd, kd, vd, scale=scale, out_dtype=out_dtype, workspace=ws, force_split=True)
+    O2, L2 = attn_block_fwd(qd, kd, vd, scale=scale, out_dtype=out_dtype, workspace=ws,
+                            force_split=True)
+    Op, Lp = attn_block_fwd(qd, kd, vd, scale=scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(L, L2), "split launch is not deterministic"
+    assert counters_zero(ws, B, H, Nq), "arrival counters not reset"
+    # The combine rounds differently from the one-workgroup path, so some
+    # outputs must differ: this shows the split launch ran.
+    assert not (torch.equal(O, Op) and torch.equal(L, Lp)), "split launch was not taken"
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale)
+    assert_bf16_close(to_f64(O), Or, "split O")
+    assert_bf16_close(to_f64(L), Lr, "split LSE")
+
+
+def test_plain_grid_shape_runs_unsplit():
+    """768 query tiles fill three waves of 256 CUs: the workspace call takes
+    the plain path and matches attn_block_fwd bit for bit."""
+    q, k, v = inputs.attn_inputs(1, 24, 8192, 300, 128, "bf16", seed=11)
+    q, k, v = dev(q), dev(k), dev(v)
+    say("case split not taken")
+    ws = attn_block_workspace(q, k)
+    O, L = attn_block_fwd(q, k, v, workspace=ws, force_split=True)
+    Op, Lp = attn_block_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Op) and torch.equal(L, Lp)
+
+
+def test_short_block_runs_unsplit_by_default():
+    """Without the force flag a 2048-key block keeps the plain grid."""
+    q, k, v = inputs.attn_inputs(1, 24, 2048, 2048, 128, "bf16", seed=12)
+    q, k, v = dev(q), dev(k), dev(v)
+    say("case split default short")
+    ws = attn_block_workspace(q, k)
+    O, L = attn_block_fwd(q, k, v, workspace=ws)
+    Op, Lp = attn_block_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Op) and torch.equal(L, Lp)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_long_block_splits_by_default_sampled_rows(out_dtype):
+    """160 query tiles against 6200 keys (97 tiles, ragged): the default
+    choice splits; sampled rows of every head against the oracle."""
+    B, H, Nq, Nkv, d = 1, 20, 2048, 6200, 128
+    q, k, v = inputs.attn_inputs(B, H, Nq, Nkv, d, "bf16", seed=21)
+    scale = inputs.default_scale(d)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    say("case split default long", out_dtype)
+    ws = attn_block_workspace(qd, kd)
+    O, L = attn_block_fwd(qd, kd, vd, scale=scale, out_dtype=out_dtype, workspace=ws)
+    Op, Lp = attn_block_fwd(qd, kd, vd, scale=scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert counters_zero(ws, B, H, Nq)
+    assert not (torch.equal(O, Op) and torch.equal(L, Lp)), "split launch was not taken"
+    rng = np.random.default_rng(22)
+    rows = np.unique(np.concatenate([[0, 255, 256, 2047], rng.choice(Nq, 40, replace=False)]))
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale, rows=rows)
+    assert_bf16_close(to_f64(O[:, :, rows]), Or, "long split O (sampled rows)")
+    assert_bf16_close(to_f64(L[:, :, rows]), Lr, "long split LSE (sampled rows)")
+
+
+@pytest.mark.parametrize("acc_dtype", [torch.float32, torch.bfloat16])
+def test_ring_2048px_split_fused(acc_dtype):
+    """The ring share (8 KV blocks of 2048 keys, 24 heads, 2048 queries) with
+    the merge fused and the split launch, from an empty accumulator whose O
+    is NaN, against attention over all 16384 keys."""
+    w = inputs.ring_2048px()
+    q = dev(w["q"])
+    B, H, Nq, d = q.shape
+    o_acc = torch.full((B, H, Nq, d), float("nan"), dtype=acc_dtype, device="cuda:0")
+    l_acc = torch.full((B, H, Nq), -float("inf"), device="cuda:0")
+    ws = attn_block_workspace(q, dev(w["ks"][0]))
+    say("case ring split fused", acc_dtype)
+    for kj, vj in zip(w["ks"], w["vs"]):
+        attn_block_fwd_merge(q, dev(kj), dev(vj), o_acc, l_acc, scale=w["scale"], workspace=ws,
+                             force_split=True)
+    torch.cuda.synchronize()
+    assert counters_zero(ws, B, H, Nq)
+    K = torch.cat(w["ks"], dim=2)
+    V = torch.cat(w["vs"], dim=2)
+    Or, Lr = oracle.ref_attn(to_oracle(w["q"]), to_oracle(K), to_oracle(V), w["scale"])
+    assert_bf16_close(to_f64(o_acc), Or, "ring split fused O")
+    assert_bf16_close(to_f64(l_acc), Lr, "ring split fused LSE")
+
+
+def test_workspace_reused_by_a_smaller_call():
+    """A workspace sized for the ring share serves a smaller split call next."""
+    B, H, Nq, Nkv, d = 1, 24, 2048, 2048, 128
+    q, k, v = inputs.attn_inputs(B, H, Nq, Nkv, d, "bf16", seed=5)
+    q2, k2, v2 = inputs.attn_inputs(1, 20, 2048, 1000, 128, "bf16", seed=6)
+    ws = attn_block_workspace(dev(q), dev(k))
+    say("case split workspace reuse")
+    attn_block_fwd(dev(q), dev(k), dev(v), out_dtype=torch.float32, workspace=ws, force_split=True)
+    O, L = attn_block_fwd(dev(q2), dev(k2), dev(v2), out_dtype=torch.float32, workspace=ws,
+                          force_split=True)
+    torch.cuda.synchronize()
+    assert counters_zero(ws, B, H, Nq)
+    Or, Lr = oracle.ref_attn(to_oracle(q2), to_oracle(k2), to_oracle(v2), inputs.default_scale(128))
+    assert_bf16_close(to_f64(O), Or, "reuse O")
+    assert_bf16_close(to_f64(L), Lr, "reuse LSE")
+
+
+def test_fp32_inputs_ignore_the_workspace():
+    q, k, v = inputs.attn_inputs(1, 24, 2048, 300, 64, "f32", seed=9)
+    q, k, v = dev(q), dev(k), dev(v)
+    say("case split f32 inputs")
+    ws = attn_block_workspace(q, k)
+    O, L = attn_block_fwd(q, k, v, workspace=ws, force_split=True)
+    Op, Lp = attn_block_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Op) and torch.equal(L, Lp)
+    assert load() is not None
