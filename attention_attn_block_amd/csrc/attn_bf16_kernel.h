@@ -286,190 +286,154 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   for (int c = 0; c < G::kChunks; ++c) k_unit[c] = l32 * G::kOct + (((2 * c + hi) ^ sk) % G::kOct);
 
   while (u < u_end) {
-  // One piece: key tiles [t_beg, t_end) of query tile `item`.
-  const int item = (int)(u / n_all);
-  const int t_beg = (int)(u - (long long)item * n_all);
-  const int t_end = (int)(u_end - u < (long long)(n_all - t_beg) ? t_beg + (u_end - u) : n_all);
-  u += t_end - t_beg;
-  const int bh = item / n_qtiles;
-  const int qt = item - bh * n_qtiles;
-  const int kvb = t_beg * kBc;  // first key of the piece
+    // One piece: key tiles [t_beg, t_end) of query tile `item`.
+    const int item = (int)(u / n_all);
+    const int t_beg = (int)(u - (long long)item * n_all);
+    const int t_end = (int)(u_end - u < (long long)(n_all - t_beg) ? t_beg + (u_end - u) : n_all);
+    u += t_end - t_beg;
+    const int bh = item / n_qtiles;
+    const int qt = item - bh * n_qtiles;
+    const int kvb = t_beg * kBc;  // first key of the piece
 
-  const __bf16* Qh = Q + (size_t)bh * Nq * D;
-  const __bf16* Kh = K + (size_t)bh * Nkv * D;
-  const __bf16* Vh = V + (size_t)bh * Nkv * D;
+    const __bf16* Qh = Q + (size_t)bh * Nq * D;
+    const __bf16* Kh = K + (size_t)bh * Nkv * D;
+    const __bf16* Vh = V + (size_t)bh * Nkv * D;
 
-  // Query rows of this lane, one per group; Q^T as the B operand: lane holds
-  // Q[row][16c + 8hi .. +7].
-  int my_q[NG];
-  bf16x8 qf[NG][G::kChunks];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    my_q[g] = qt * kRowsWG + (wave * NG + g) * 32 + l32;
-    const int q_ld = my_q[g] < Nq ? my_q[g] : Nq - 1;
-#pragma unroll
-    for (int c = 0; c < G::kChunks; ++c) {
-      if (G::kHalfTail && c == G::kChunks - 1 && hi) {
-        qf[g][c] = bf16x8{};
-      } else {
-        qf[g][c] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)q_ld * D + 16 * c + 8 * hi);
-      }
-    }
-  }
-
-  // S^T = K Q^T for the kBc keys of the K tile in LDS buffer `buf`; each K
-  // operand read feeds the products of all NG query groups.
-  auto qk = [&](int buf, f32x16 (*s)[kKT]) {
-#pragma unroll
-    for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-      for (int g = 0; g < NG; ++g) s[g][kt] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < G::kChunks; ++c) {
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) {
-        bf16x8 a;
-        if (G::kHalfTail && c == G::kChunks - 1 && hi) {
-          a = bf16x8{};
-        } else {
-          a = __builtin_bit_cast(bf16x8, k_lds[buf][kt * 32 * G::kOct + k_unit[c]]);
-        }
-#pragma unroll
-        for (int g = 0; g < NG; ++g) s[g][kt] = mfma32(a, qf[g][c], s[g][kt]);
-      }
-    }
-  };
-  // Keys past the end of the block (last tile only) get zero weight.
-  auto mask_tail = [&](f32x16 (*s)[kKT], int kv0) {
-    if (kv0 + kBc > Nkv) {
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= Nkv) s[g][kt][r] = -INFINITY;
-          }
-    }
-  };
-
-  // Transposing V reads (see lds_read_tr16): in lane group q = lane / 16,
-  // lane i names row 4 (q / 2) + i / 4 of each 8-key half chunk and columns
-  // 16 (q % 2) + 4 (i % 4) .. +3 of each 32-column d tile.  The row's swizzle
-  // depends on i / 4 only, so each d tile gets one lane-constant offset.
-  const int vq = lane >> 4, vi = lane & 15;
-  const int v_row = 4 * (vq >> 1) + (vi >> 2);
-  const int sv = swz_v<G::kOct>(v_row);
-  int v_off[G::kDTiles];  // bf16 element offsets inside a V buffer
-#pragma unroll
-  for (int dt = 0; dt < G::kDTiles; ++dt) {
-    const int unit = 4 * dt + 2 * (vq & 1) + ((vi & 3) >> 1);
-    v_off[dt] = (v_row * G::kOct + (unit ^ sv)) * 8 + 4 * (vi & 1);
-  }
-
-  f32x16 acc[NG][G::kDTiles];
-#pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int t = 0; t < G::kDTiles; ++t) acc[g][t] = f32x16{};
-  float l_run[NG];   // this lane's share of each row's normaliser (bf16 weights)
-  float m_ref[NG];   // reference row max for the exponentials, log2 units
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-  const int n_tiles = t_end - t_beg;  // key tiles of this piece
-
-  // Ping-pong schedule.  Waves w and w + 4 share a SIMD.  Group A (waves 0-3)
-  // and group B (waves 4-7) run the same per-wave pipeline one slot apart, so
-  // while one wave of a SIMD is in its matrix phase the other is in its vector
-  // phase.  Per tile t a wave runs
-  //   M(t):   S(t+1) = K(t+1) Q^T and O^T += V(t)^T P(t)^T  (matrix cores, LDS)
-  //   W(t+1): exponent form, weights P(t+1), normaliser, rare rescale  (VALU)
-  // Group A runs M(k) in slot 2k and W(k+1) in slot 2k+1; group B runs M(k) in
-  // slot 2k+1 and W(k+1) in slot 2k+2.  Every slot ends with a barrier that
-  // every wave executes (the slot count is the same for the whole workgroup).
-  // K(t) and V(t) live in LDS buffer t % 2.  Slot 2k starts the loads of
-  // K(k+2) and V(k+1) into the buffers whose last readers ran in slot 2k-1;
-  // slot 2k+1 ends by waiting for them.
-  const int grp = wave >> 2;
-  if (grp == 1) {
-    dma_tile(IsK{}, Kh, k_lds[0], kvb);
-    dma_tile(IsV{}, Vh, v_lds[0], kvb);
-    if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kvb + kBc);
-  }
-  dma_wait();
-  __syncthreads();
-
-  f32x16 s_nxt[NG][kKT];
-  bf16x8 pb[NG][kCH];
-  qk(0, s_nxt);
-  // Slot 0 loads K tile 2 into the buffer tile 0 was just read from: every
-  // wave must have finished those reads first.
-  __syncthreads();
-
-  // W(t): scores of tile t (raw, in s_nxt) -> weights pb, normaliser share.
-  auto w_phase = [&](int t) __attribute__((always_inline)) {
-    mask_tail(s_nxt, kvb + t * kBc);
+    // Query rows of this lane, one per group; Q^T as the B operand: lane holds
+    // Q[row][16c + 8hi .. +7].
+    int my_q[NG];
+    bf16x8 qf[NG][G::kChunks];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      if (t == 0) {  // reference max from tile 0
-        l_run[g] = 0.f;
-        m_ref[g] = max_with_partner32(row_max(s_nxt[g])) * c2;
+      my_q[g] = qt * kRowsWG + (wave * NG + g) * 32 + l32;
+      const int q_ld = my_q[g] < Nq ? my_q[g] : Nq - 1;
+#pragma unroll
+      for (int c = 0; c < G::kChunks; ++c) {
+        if (G::kHalfTail && c == G::kChunks - 1 && hi) {
+          qf[g][c] = bf16x8{};
+        } else {
+          qf[g][c] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)q_ld * D + 16 * c + 8 * hi);
+        }
       }
-      const float neg_m = -m_ref[g];
+    }
+
+    // S^T = K Q^T for the kBc keys of the K tile in LDS buffer `buf`; each K
+    // operand read feeds the products of all NG query groups.
+    auto qk = [&](int buf, f32x16 (*s)[kKT]) {
 #pragma unroll
       for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s_nxt[g][kt][r] = fmaf(s_nxt[g][kt][r], c2, neg_m);
-    }
-    float ls[NG];
+        for (int g = 0; g < NG; ++g) s[g][kt] = f32x16{};
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
+      for (int c = 0; c < G::kChunks; ++c) {
 #pragma unroll
-      for (int ch = 0; ch < kCH; ++ch)
+        for (int kt = 0; kt < kKT; ++kt) {
+          bf16x8 a;
+          if (G::kHalfTail && c == G::kChunks - 1 && hi) {
+            a = bf16x8{};
+          } else {
+            a = __builtin_bit_cast(bf16x8, k_lds[buf][kt * 32 * G::kOct + k_unit[c]]);
+          }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          pb[g][ch][j] = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
-      // The normaliser sums the same bf16 weights the product uses; this
-      // lane's share of it also bounds every weight the lane holds.
-      float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-      for (int ch = 0; ch < kCH; ++ch) {
-        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][0], pb[g][ch][1]}, ones, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][2], pb[g][ch][3]}, ones, ls1, false);
-        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][4], pb[g][ch][5]}, ones, ls0, false);
-        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][6], pb[g][ch][7]}, ones, ls1, false);
+          for (int g = 0; g < NG; ++g) s[g][kt] = mfma32(a, qf[g][c], s[g][kt]);
+        }
       }
-      ls[g] = ls0 + ls1;
-    }
-    // Rare: a lane's share of a row's sum exceeds the limit (so some weight
-    // there exceeds 2^9), i.e. the row's scores grew well past its reference
-    // max.  Rows whose tile max exceeds the reference by more than kTau move
-    // the reference to it, rescale what they accumulated and recompute this
-    // tile's weights.
-    bool any_big = false;
+    };
+    // Keys past the end of the block (last tile only) get zero weight.
+    auto mask_tail = [&](f32x16 (*s)[kKT], int kv0) {
+      if (kv0 + kBc > Nkv) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) any_big |= !(ls[g] <= kLaneSumLimit);
-    if (__builtin_amdgcn_ballot_w64(any_big)) {
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kv0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+              if (key >= Nkv) s[g][kt][r] = -INFINITY;
+            }
+      }
+    };
+
+    // Transposing V reads (see lds_read_tr16): in lane group q = lane / 16,
+    // lane i names row 4 (q / 2) + i / 4 of each 8-key half chunk and columns
+    // 16 (q % 2) + 4 (i % 4) .. +3 of each 32-column d tile.  The row's swizzle
+    // depends on i / 4 only, so each d tile gets one lane-constant offset.
+    const int vq = lane >> 4, vi = lane & 15;
+    const int v_row = 4 * (vq >> 1) + (vi >> 2);
+    const int sv = swz_v<G::kOct>(v_row);
+    int v_off[G::kDTiles];  // bf16 element offsets inside a V buffer
+#pragma unroll
+    for (int dt = 0; dt < G::kDTiles; ++dt) {
+      const int unit = 4 * dt + 2 * (vq & 1) + ((vi & 3) >> 1);
+      v_off[dt] = (v_row * G::kOct + (unit ^ sv)) * 8 + 4 * (vi & 1);
+    }
+
+    f32x16 acc[NG][G::kDTiles];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int t = 0; t < G::kDTiles; ++t) acc[g][t] = f32x16{};
+    float l_run[NG];   // this lane's share of each row's normaliser (bf16 weights)
+    float m_ref[NG];   // reference row max for the exponentials, log2 units
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    const int n_tiles = t_end - t_beg;  // key tiles of this piece
+
+    // Ping-pong schedule.  Waves w and w + 4 share a SIMD.  Group A (waves 0-3)
+    // and group B (waves 4-7) run the same per-wave pipeline one slot apart, so
+    // while one wave of a SIMD is in its matrix phase the other is in its vector
+    // phase.  Per tile t a wave runs
+    //   M(t):   S(t+1) = K(t+1) Q^T and O^T += V(t)^T P(t)^T  (matrix cores, LDS)
+    //   W(t+1): exponent form, weights P(t+1), normaliser, rare rescale  (VALU)
+    // Group A runs M(k) in slot 2k and W(k+1) in slot 2k+1; group B runs M(k) in
+    // slot 2k+1 and W(k+1) in slot 2k+2.  Every slot ends with a barrier that
+    // every wave executes (the slot count is the same for the whole workgroup).
+    // K(t) and V(t) live in LDS buffer t % 2.  Slot 2k starts the loads of
+    // K(k+2) and V(k+1) into the buffers whose last readers ran in slot 2k-1;
+    // slot 2k+1 ends by waiting for them.
+    const int grp = wave >> 2;
+    if (grp == 1) {
+      dma_tile(IsK{}, Kh, k_lds[0], kvb);
+      dma_tile(IsV{}, Vh, v_lds[0], kvb);
+      if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kvb + kBc);
+    }
+    dma_wait();
+    __syncthreads();
+
+    f32x16 s_nxt[NG][kKT];
+    bf16x8 pb[NG][kCH];
+    qk(0, s_nxt);
+    // Slot 0 loads K tile 2 into the buffer tile 0 was just read from: every
+    // wave must have finished those reads first.
+    __syncthreads();
+
+    // W(t): scores of tile t (raw, in s_nxt) -> weights pb, normaliser share.
+    auto w_phase = [&](int t) __attribute__((always_inline)) {
+      mask_tail(s_nxt, kvb + t * kBc);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float mx = max_with_partner32(row_max(s_nxt[g]));
-        const bool grow = mx > kTau;
-        const float delta = grow ? mx : 0.f;
-        const float alpha = fast_exp2(-delta);
-        l_run[g] *= alpha;
+        if (t == 0) {  // reference max from tile 0
+          l_run[g] = 0.f;
+          m_ref[g] = max_with_partner32(row_max(s_nxt[g])) * c2;
+        }
+        const float neg_m = -m_ref[g];
 #pragma unroll
-        for (int dt = 0; dt < G::kDTiles; ++dt)
+        for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[g][dt][r] *= alpha;
-        m_ref[g] += delta;
+          for (int r = 0; r < 16; ++r) s_nxt[g][kt][r] = fmaf(s_nxt[g][kt][r], c2, neg_m);
+      }
+      float ls[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+#pragma unroll
+        for (int ch = 0; ch < kCH; ++ch)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            pb[g][ch][j] = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
+        // The normaliser sums the same bf16 weights the product uses; this
+        // lane's share of it also bounds every weight the lane holds.
         float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
         for (int ch = 0; ch < kCH; ++ch) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const __bf16 re = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j] - delta);
-            pb[g][ch][j] = grow ? re : pb[g][ch][j];
-          }
           ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][0], pb[g][ch][1]}, ones, ls0, false);
           ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][2], pb[g][ch][3]}, ones, ls1, false);
           ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][4], pb[g][ch][5]}, ones, ls0, false);
@@ -477,374 +441,412 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
         }
         ls[g] = ls0 + ls1;
       }
-    }
+      // Rare: a lane's share of a row's sum exceeds the limit (so some weight
+      // there exceeds 2^9), i.e. the row's scores grew well past its reference
+      // max.  Rows whose tile max exceeds the reference by more than kTau move
+      // the reference to it, rescale what they accumulated and recompute this
+      // tile's weights.
+      bool any_big = false;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) l_run[g] += ls[g];
-  };
+      for (int g = 0; g < NG; ++g) any_big |= !(ls[g] <= kLaneSumLimit);
+      if (__builtin_amdgcn_ballot_w64(any_big)) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const float mx = max_with_partner32(row_max(s_nxt[g]));
+          const bool grow = mx > kTau;
+          const float delta = grow ? mx : 0.f;
+          const float alpha = fast_exp2(-delta);
+          l_run[g] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[g][dt][r] *= alpha;
+          m_ref[g] += delta;
+          float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+          for (int ch = 0; ch < kCH; ++ch) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const __bf16 re = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j] - delta);
+              pb[g][ch][j] = grow ? re : pb[g][ch][j];
+            }
+            ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][0], pb[g][ch][1]}, ones, ls0, false);
+            ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][2], pb[g][ch][3]}, ones, ls1, false);
+            ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][4], pb[g][ch][5]}, ones, ls0, false);
+            ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][6], pb[g][ch][7]}, ones, ls1, false);
+          }
+          ls[g] = ls0 + ls1;
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) l_run[g] += ls[g];
+    };
 
-  // M(t) with K(t+1) in buffer kb and V(t) in buffer vb (compile-time).
-  auto m_phase = [&](auto kb_c, auto vb_c, int t) __attribute__((always_inline)) {
-    constexpr int kb = decltype(kb_c)::value, vbi = decltype(vb_c)::value;
-    __builtin_amdgcn_s_setprio(1);
-    if (t + 1 < n_tiles) {
-      // S^T = K Q^T for tile t + 1; K-operand reads kKD products ahead, the
-      // two 32-key accumulators alternate.
-      constexpr int kQK = kKT * G::kChunks;
-      constexpr int kKD = kKDepth;
-      bf16x8 kr[kQK];
-      auto kread = [&](int i) -> bf16x8 {
-        const int c = i / kKT, kt = i % kKT;
-        if (G::kHalfTail && c == G::kChunks - 1 && hi) return bf16x8{};
-        return __builtin_bit_cast(bf16x8, k_lds[kb][kt * 32 * G::kOct + k_unit[c]]);
+    // M(t) with K(t+1) in buffer kb and V(t) in buffer vb (compile-time).
+    auto m_phase = [&](auto kb_c, auto vb_c, int t) __attribute__((always_inline)) {
+      constexpr int kb = decltype(kb_c)::value, vbi = decltype(vb_c)::value;
+      __builtin_amdgcn_s_setprio(1);
+      if (t + 1 < n_tiles) {
+        // S^T = K Q^T for tile t + 1; K-operand reads kKD products ahead, the
+        // two 32-key accumulators alternate.
+        constexpr int kQK = kKT * G::kChunks;
+        constexpr int kKD = kKDepth;
+        bf16x8 kr[kQK];
+        auto kread = [&](int i) -> bf16x8 {
+          const int c = i / kKT, kt = i % kKT;
+          if (G::kHalfTail && c == G::kChunks - 1 && hi) return bf16x8{};
+          return __builtin_bit_cast(bf16x8, k_lds[kb][kt * 32 * G::kOct + k_unit[c]]);
+        };
+#pragma unroll
+        for (int i = 0; i < kKD && i < kQK; ++i) kr[i] = kread(i);
+        __builtin_amdgcn_sched_group_barrier(0x100, kKD, 0);
+#pragma unroll
+        for (int i = 0; i < kQK; ++i) {
+          if (i + kKD < kQK) kr[i + kKD] = kread(i + kKD);
+          const int c = i / kKT, kt = i % kKT;
+#pragma unroll
+          for (int g = 0; g < NG; ++g)
+            s_nxt[g][kt] = mfma32(kr[i], qf[g][c], c == 0 ? f32x16{} : s_nxt[g][kt]);
+          if (i + kKD < kQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);                    // MFMA
+        }
+      }
+      // O^T += V^T P^T for tile t (16 keys per product).  Slot j of half-wave h
+      // holds key 8 (j / 4) + 4 h + j % 4 of the chunk on both operands; the
+      // two transposing reads of a product are issued kVD products ahead.
+      const __bf16* vbase = reinterpret_cast<const __bf16*>(v_lds[vbi]);
+      constexpr int kPV = kCH * G::kDTiles;
+      constexpr int kVD = kVDepth;
+      bf16x8 vr[kPV];
+      auto vread = [&](int j) -> bf16x8 {
+        const int ch = j / G::kDTiles, dt = j % G::kDTiles;
+        const __bf16* vp = vbase + v_off[dt] + 16 * ch * G::kOct * 8;
+        const bf16x4 lo = lds_read_tr16(vp);
+        const bf16x4 up = lds_read_tr16(vp + 8 * G::kOct * 8);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
       };
 #pragma unroll
-      for (int i = 0; i < kKD && i < kQK; ++i) kr[i] = kread(i);
-      __builtin_amdgcn_sched_group_barrier(0x100, kKD, 0);
+      for (int j = 0; j < kVD && j < kPV; ++j) vr[j] = vread(j);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVD, 1);
 #pragma unroll
-      for (int i = 0; i < kQK; ++i) {
-        if (i + kKD < kQK) kr[i + kKD] = kread(i + kKD);
-        const int c = i / kKT, kt = i % kKT;
+      for (int j = 0; j < kPV; ++j) {
+        if (j + kVD < kPV) vr[j + kVD] = vread(j + kVD);
+        const int ch = j / G::kDTiles, dt = j % G::kDTiles;
 #pragma unroll
-        for (int g = 0; g < NG; ++g) s_nxt[g][kt] = mfma32(kr[i], qf[g][c], c == 0 ? f32x16{} : s_nxt[g][kt]);
-        if (i + kKD < kQK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);                    // MFMA
+        for (int g = 0; g < NG; ++g) acc[g][dt] = mfma32(vr[j], pb[g][ch], acc[g][dt]);
+        if (j + kVD < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, NG, 1);                    // MFMA
       }
-    }
-    // O^T += V^T P^T for tile t (16 keys per product).  Slot j of half-wave h
-    // holds key 8 (j / 4) + 4 h + j % 4 of the chunk on both operands; the
-    // two transposing reads of a product are issued kVD products ahead.
-    const __bf16* vbase = reinterpret_cast<const __bf16*>(v_lds[vbi]);
-    constexpr int kPV = kCH * G::kDTiles;
-    constexpr int kVD = kVDepth;
-    bf16x8 vr[kPV];
-    auto vread = [&](int j) -> bf16x8 {
-      const int ch = j / G::kDTiles, dt = j % G::kDTiles;
-      const __bf16* vp = vbase + v_off[dt] + 16 * ch * G::kOct * 8;
-      const bf16x4 lo = lds_read_tr16(vp);
-      const bf16x4 up = lds_read_tr16(vp + 8 * G::kOct * 8);
-      return bf16x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+      __builtin_amdgcn_s_setprio(0);
     };
-#pragma unroll
-    for (int j = 0; j < kVD && j < kPV; ++j) vr[j] = vread(j);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVD, 1);
-#pragma unroll
-    for (int j = 0; j < kPV; ++j) {
-      if (j + kVD < kPV) vr[j + kVD] = vread(j + kVD);
-      const int ch = j / G::kDTiles, dt = j % G::kDTiles;
-#pragma unroll
-      for (int g = 0; g < NG; ++g) acc[g][dt] = mfma32(vr[j], pb[g][ch], acc[g][dt]);
-      if (j + kVD < kPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, NG, 1);                    // MFMA
-    }
-    __builtin_amdgcn_s_setprio(0);
-  };
 
-  w_phase(0);
+    w_phase(0);
 
-  // One slot; p = slot index mod 4 (compile-time), so the buffer of every
-  // tile a slot touches is known: in slots 4j + {0, 1} tile k is even, in
-  // slots 4j + {2, 3} odd (k = slot / 2 rounded down).
-  auto run_slot = [&](auto p_c, int s) __attribute__((always_inline)) {
-    constexpr int p = decltype(p_c)::value;
-    constexpr int kpar = p >> 1;  // parity of k
-    using KP = std::integral_constant<int, kpar>;
-    using KQ = std::integral_constant<int, kpar ^ 1>;
-    const int k = s >> 1;
-    if constexpr ((p & 1) == 0) {
-      if (grp == 1) {  // group B is in its vector phase in even slots
-        if (k + 2 < n_tiles) dma_tile(IsK{}, Kh, k_lds[kpar], kvb + (k + 2) * kBc);
-        if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], kvb + (k + 1) * kBc);
-      }
-      if (grp == 0) {
-        if (k < n_tiles) m_phase(KQ{}, KP{}, k);
-      } else {
-        if (k >= 1 && k < n_tiles) w_phase(k);
-      }
-    } else {
-      if (grp == 0) {
-        if (k + 1 < n_tiles) w_phase(k + 1);
-      } else {
-        if (k < n_tiles) m_phase(KQ{}, KP{}, k);
-      }
-      dma_wait();
-    }
-    __syncthreads();
-  };
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  using P2 = std::integral_constant<int, 2>;
-  using P3 = std::integral_constant<int, 3>;
-  for (int s = 0; s < 2 * n_tiles; s += 4) {
-    run_slot(P0{}, s);
-    run_slot(P1{}, s + 1);
-    run_slot(P2{}, s + 2);
-    run_slot(P3{}, s + 3);
-  }
-
-  if (!SPLIT || (t_beg == 0 && t_end == n_all)) {
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const float l_tot = sum_with_partner32(l_run[g]);
-      if (my_q[g] < Nq) {
-        // This block's partial: O_b = acc / l_tot, LSE_b = m_ref + log2 l_tot
-        // (log2 units).  MERGE folds it into the running (Out, LSE) of the row
-        // with the log-sum-exp identity; LSE = -inf there marks an empty
-        // accumulator whose O is not read.
-        const size_t lrow = (size_t)bh * Nq + my_q[g];
-        const float lse_b = m_ref[g] + fast_log2(l_tot);
-        float wb = 1.f / l_tot, wa = 0.f, lse_new = lse_b;
-        bool has_a = false;
-        if constexpr (MERGE) {
-          const float la = LSE[lrow] * kLog2e;
-          has_a = la != -INFINITY;
-          if (has_a) {
-            const float m = fmaxf(la, lse_b);
-            const float ea = fast_exp2(la - m), eb = fast_exp2(lse_b - m);
-            const float inv = 1.f / (ea + eb);
-            wa = ea * inv;
-            wb = eb * inv / l_tot;
-            lse_new = m + fast_log2(ea + eb);
-          }
+    // One slot; p = slot index mod 4 (compile-time), so the buffer of every
+    // tile a slot touches is known: in slots 4j + {0, 1} tile k is even, in
+    // slots 4j + {2, 3} odd (k = slot / 2 rounded down).
+    auto run_slot = [&](auto p_c, int s) __attribute__((always_inline)) {
+      constexpr int p = decltype(p_c)::value;
+      constexpr int kpar = p >> 1;  // parity of k
+      using KP = std::integral_constant<int, kpar>;
+      using KQ = std::integral_constant<int, kpar ^ 1>;
+      const int k = s >> 1;
+      if constexpr ((p & 1) == 0) {
+        if (grp == 1) {  // group B is in its vector phase in even slots
+          if (k + 2 < n_tiles) dma_tile(IsK{}, Kh, k_lds[kpar], kvb + (k + 2) * kBc);
+          if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], kvb + (k + 1) * kBc);
         }
-        const size_t orow = lrow * D;
-#pragma unroll
-        for (int dt = 0; dt < G::kDTiles; ++dt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int d0 = dt * 32 + 8 * q4 + 4 * hi;
-            if (d0 < D) {
-              float o[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) o[e] = acc[g][dt][4 * q4 + e] * wb;
-              if constexpr (OUT_F32) {
-                f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
-                if (MERGE && has_a) {
-                  const f32x4 a = *p;
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], o[e]);
-                }
-                *p = f32x4{o[0], o[1], o[2], o[3]};
-              } else {
-                bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
-                if (MERGE && has_a) {
-                  const bf16x4 a = *p;
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], o[e]);
-                }
-                *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-              }
-            }
-          }
-        if (hi == 0) LSE[lrow] = lse_new * kLn2;
+        if (grp == 0) {
+          if (k < n_tiles) m_phase(KQ{}, KP{}, k);
+        } else {
+          if (k >= 1 && k < n_tiles) w_phase(k);
+        }
+      } else {
+        if (grp == 0) {
+          if (k + 1 < n_tiles) w_phase(k + 1);
+        } else {
+          if (k < n_tiles) m_phase(KQ{}, KP{}, k);
+        }
+        dma_wait();
       }
-    }
-  } else {
-    // One of the k (2..kMaxPieces) pieces of a query tile whose key range
-    // is cut between workgroups; piece j holds the j-th key range.  All
-    // partials take one representation -- O normalised, in fp32, and LSE in
-    // log2 units -- and are combined in key order, so the result is the same
-    // bits whichever piece combines.
-    constexpr int kSlot = kRowsWG * (D + 1);  // floats per partial: O rows, then LSE
-    const long long total = (long long)n_items * n_all;
-    // Workgroup whose range holds unit x (ranges start at total * w / nblk).
-    auto owner = [&](long long x) { return ((x + 1) * nblk + total - 1) / total - 1; };
-    const long long w_first = owner((long long)item * n_all);
-    const int n_pieces = (int)(owner((long long)item * n_all + n_all - 1) - w_first + 1);
-    const int j_piece = (int)(logical - w_first);
-    float* slots = ws_part + (size_t)item * kMaxPieces * kSlot;
-    float lse_own[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const float l_tot = sum_with_partner32(l_run[g]);
-      lse_own[g] = m_ref[g] + fast_log2(l_tot);
-      const float inv = 1.f / l_tot;
-#pragma unroll
-      for (int dt = 0; dt < G::kDTiles; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[g][dt][r] *= inv;
-    }
-    // Partials are written and read with device-coherent buffer accesses
-    // (sc1, the encoding of device-scope atomic loads and stores: coherent
-    // across the per-XCD L2s), so the exchange needs no L2 write-back or
-    // invalidate -- those would also drop the K/V tiles other workgroups are
-    // reusing from L2.
-    auto slot_rsrc = [&](int j) {
-      return __builtin_amdgcn_make_buffer_rsrc(slots + (size_t)j * kSlot, (short)0, kSlot * 4,
-                                               kBufferFlags);
+      __syncthreads();
     };
-    constexpr int kCoherent = 16;  // sc1
-    auto publish = [&]() {
-      const __amdgpu_buffer_rsrc_t own = slot_rsrc(j_piece);
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    for (int s = 0; s < 2 * n_tiles; s += 4) {
+      run_slot(P0{}, s);
+      run_slot(P1{}, s + 1);
+      run_slot(P2{}, s + 2);
+      run_slot(P3{}, s + 3);
+    }
+
+    if (!SPLIT || (t_beg == 0 && t_end == n_all)) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        if (my_q[g] >= Nq) continue;
-        const int row = (wave * NG + g) * 32 + l32;
+        const float l_tot = sum_with_partner32(l_run[g]);
+        if (my_q[g] < Nq) {
+          // This block's partial: O_b = acc / l_tot, LSE_b = m_ref + log2 l_tot
+          // (log2 units).  MERGE folds it into the running (Out, LSE) of the row
+          // with the log-sum-exp identity; LSE = -inf there marks an empty
+          // accumulator whose O is not read.
+          const size_t lrow = (size_t)bh * Nq + my_q[g];
+          const float lse_b = m_ref[g] + fast_log2(l_tot);
+          float wb = 1.f / l_tot, wa = 0.f, lse_new = lse_b;
+          bool has_a = false;
+          if constexpr (MERGE) {
+            const float la = LSE[lrow] * kLog2e;
+            has_a = la != -INFINITY;
+            if (has_a) {
+              const float m = fmaxf(la, lse_b);
+              const float ea = fast_exp2(la - m), eb = fast_exp2(lse_b - m);
+              const float inv = 1.f / (ea + eb);
+              wa = ea * inv;
+              wb = eb * inv / l_tot;
+              lse_new = m + fast_log2(ea + eb);
+            }
+          }
+          const size_t orow = lrow * D;
+#pragma unroll
+          for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+              if (d0 < D) {
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = acc[g][dt][4 * q4 + e] * wb;
+                if constexpr (OUT_F32) {
+                  f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
+                  if (MERGE && has_a) {
+                    const f32x4 a = *p;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], o[e]);
+                  }
+                  *p = f32x4{o[0], o[1], o[2], o[3]};
+                } else {
+                  bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
+                  if (MERGE && has_a) {
+                    const bf16x4 a = *p;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], o[e]);
+                  }
+                  *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+                }
+              }
+            }
+          if (hi == 0) LSE[lrow] = lse_new * kLn2;
+        }
+      }
+    } else {
+      // One of the k (2..kMaxPieces) pieces of a query tile whose key range
+      // is cut between workgroups; piece j holds the j-th key range.  All
+      // partials take one representation -- O normalised, in fp32, and LSE in
+      // log2 units -- and are combined in key order, so the result is the same
+      // bits whichever piece combines.
+      constexpr int kSlot = kRowsWG * (D + 1);  // floats per partial: O rows, then LSE
+      const long long total = (long long)n_items * n_all;
+      // Workgroup whose range holds unit x (ranges start at total * w / nblk).
+      auto owner = [&](long long x) { return ((x + 1) * nblk + total - 1) / total - 1; };
+      const long long w_first = owner((long long)item * n_all);
+      const int n_pieces = (int)(owner((long long)item * n_all + n_all - 1) - w_first + 1);
+      const int j_piece = (int)(logical - w_first);
+      float* slots = ws_part + (size_t)item * kMaxPieces * kSlot;
+      float lse_own[NG];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float l_tot = sum_with_partner32(l_run[g]);
+        lse_own[g] = m_ref[g] + fast_log2(l_tot);
+        const float inv = 1.f / l_tot;
 #pragma unroll
         for (int dt = 0; dt < G::kDTiles; ++dt)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int d0 = dt * 32 + 8 * q4 + 4 * hi;
-            if (d0 < D)
-              __builtin_amdgcn_raw_buffer_store_b128(
-                  __builtin_bit_cast(u32x4, f32x4{acc[g][dt][4 * q4], acc[g][dt][4 * q4 + 1],
-                                                  acc[g][dt][4 * q4 + 2], acc[g][dt][4 * q4 + 3]}),
-                  own, (row * D + d0) * 4, 0, kCoherent);
-          }
-        if (hi == 0)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_own[g]), own,
-                                                (kRowsWG * D + row) * 4, 0, kCoherent);
+          for (int r = 0; r < 16; ++r) acc[g][dt][r] *= inv;
       }
-    };
-    // Arrival on the tile's counter (0 before the first piece arrives; the
-    // combining piece sets it back to 0).  The low 16 bits count arrivals,
-    // bit 16 says piece 0 has published.
-    //   piece j > 0: publish, add 1; combine iff the counter was
-    //                2^16 + (k - 1) (piece 0 published, every other piece in).
-    //   piece 0:     add 1; combine iff it was k - 1 (every other piece has
-    //                published).  Otherwise publish, add 2^16, and combine iff
-    //                the arrivals then numbered k.
-    // Piece 0 ends its workgroup's range and usually arrives last, so it
-    // usually combines without publishing.  Exactly one piece combines, only
-    // after every other partial is published, and no workgroup ever waits
-    // for another.  The counter is a relaxed device-scope atomic; each
-    // arrival first waits until this workgroup's coherent stores are
-    // acknowledged.
-    unsigned* cnt = ws_count + item;
-    auto arrive = [&](unsigned add) -> unsigned {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own published stores acknowledged
-      __syncthreads();
-      if (tid == 0)
-        s_arrive = __hip_atomic_fetch_add(cnt, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      return s_arrive;
-    };
-    constexpr unsigned kPublished0 = 1u << 16;
-    const unsigned others = (unsigned)n_pieces - 1u;
-    bool combine;
-    if (j_piece > 0) {
-      publish();
-      combine = arrive(1u) == kPublished0 + others;
-    } else {
-      const unsigned first = arrive(1u);
-      if (first == others) {
-        combine = true;
-      } else {
+      // Partials are written and read with device-coherent buffer accesses
+      // (sc1, the encoding of device-scope atomic loads and stores: coherent
+      // across the per-XCD L2s), so the exchange needs no L2 write-back or
+      // invalidate -- those would also drop the K/V tiles other workgroups are
+      // reusing from L2.
+      auto slot_rsrc = [&](int j) {
+        return __builtin_amdgcn_make_buffer_rsrc(slots + (size_t)j * kSlot, (short)0, kSlot * 4,
+                                                 kBufferFlags);
+      };
+      constexpr int kCoherent = 16;  // sc1
+      auto publish = [&]() {
+        const __amdgpu_buffer_rsrc_t own = slot_rsrc(j_piece);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          if (my_q[g] >= Nq) continue;
+          const int row = (wave * NG + g) * 32 + l32;
+#pragma unroll
+          for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+              if (d0 < D)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, f32x4{acc[g][dt][4 * q4], acc[g][dt][4 * q4 + 1],
+                                                    acc[g][dt][4 * q4 + 2], acc[g][dt][4 * q4 + 3]}),
+                    own, (row * D + d0) * 4, 0, kCoherent);
+            }
+          if (hi == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_own[g]), own,
+                                                  (kRowsWG * D + row) * 4, 0, kCoherent);
+        }
+      };
+      // Arrival on the tile's counter (0 before the first piece arrives; the
+      // combining piece sets it back to 0).  The low 16 bits count arrivals,
+      // bit 16 says piece 0 has published.
+      //   piece j > 0: publish, add 1; combine iff the counter was
+      //                2^16 + (k - 1) (piece 0 published, every other piece in).
+      //   piece 0:     add 1; combine iff it was k - 1 (every other piece has
+      //                published).  Otherwise publish, add 2^16, and combine iff
+      //                the arrivals then numbered k.
+      // Piece 0 ends its workgroup's range and usually arrives last, so it
+      // usually combines without publishing.  Exactly one piece combines, only
+      // after every other partial is published, and no workgroup ever waits
+      // for another.  The counter is a relaxed device-scope atomic; each
+      // arrival first waits until this workgroup's coherent stores are
+      // acknowledged.
+      unsigned* cnt = ws_count + item;
+      auto arrive = [&](unsigned add) -> unsigned {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own published stores acknowledged
+        __syncthreads();
+        if (tid == 0)
+          s_arrive = __hip_atomic_fetch_add(cnt, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        return s_arrive;
+      };
+      constexpr unsigned kPublished0 = 1u << 16;
+      const unsigned others = (unsigned)n_pieces - 1u;
+      bool combine;
+      if (j_piece > 0) {
         publish();
-        combine = (arrive(kPublished0) & 0xffffu) == others + 1u;
+        combine = arrive(1u) == kPublished0 + others;
+      } else {
+        const unsigned first = arrive(1u);
+        if (first == others) {
+          combine = true;
+        } else {
+          publish();
+          combine = (arrive(kPublished0) & 0xffffu) == others + 1u;
+        }
       }
-    }
-    if (combine) {
-      if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (combine) {
+        if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        if (my_q[g] >= Nq) continue;
-        const int row = (wave * NG + g) * 32 + l32;
-        const size_t lrow = (size_t)bh * Nq + my_q[g];
-        // Weights of the pieces: e_j = 2^(L_j - m), normalised by their sum.
-        // Every slot of the tile is read (all are inside the workspace) and
-        // the ones that are not another piece's published partial are
-        // replaced by selects, so the loads issue back to back without
-        // branches between them.
-        float lp[kMaxPieces], wp[kMaxPieces];
+        for (int g = 0; g < NG; ++g) {
+          if (my_q[g] >= Nq) continue;
+          const int row = (wave * NG + g) * 32 + l32;
+          const size_t lrow = (size_t)bh * Nq + my_q[g];
+          // Weights of the pieces: e_j = 2^(L_j - m), normalised by their sum.
+          // Every slot of the tile is read (all are inside the workspace) and
+          // the ones that are not another piece's published partial are
+          // replaced by selects, so the loads issue back to back without
+          // branches between them.
+          float lp[kMaxPieces], wp[kMaxPieces];
 #pragma unroll
-        for (int j = 0; j < kMaxPieces; ++j)
-          lp[j] = j < n_pieces ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                     slot_rsrc(j), (kRowsWG * D + row) * 4, 0, kCoherent))
-                               : 0.f;
-        float m = -INFINITY;
+          for (int j = 0; j < kMaxPieces; ++j)
+            lp[j] = j < n_pieces ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                       slot_rsrc(j), (kRowsWG * D + row) * 4, 0, kCoherent))
+                                 : 0.f;
+          float m = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < kMaxPieces; ++j) {
-          lp[j] = j == j_piece ? lse_own[g] : (j < n_pieces ? lp[j] : -INFINITY);
-          m = fmaxf(m, lp[j]);
-        }
-        float esum = 0.f;
-#pragma unroll
-        for (int j = 0; j < kMaxPieces; ++j) {
-          wp[j] = j < n_pieces ? fast_exp2(lp[j] - m) : 0.f;
-          esum += wp[j];
-        }
-        const float einv = 1.f / esum;
-#pragma unroll
-        for (int j = 0; j < kMaxPieces; ++j) wp[j] *= einv;
-        const float lse_b = m + fast_log2(esum);
-        // Fold into the running (Out, LSE) as in the unsplit epilogue.
-        float wa = 0.f, wb = 1.f, lse_new = lse_b;
-        bool has_a = false;
-        if constexpr (MERGE) {
-          const float la = LSE[lrow] * kLog2e;
-          has_a = la != -INFINITY;
-          if (has_a) {
-            const float m2 = fmaxf(la, lse_b);
-            const float ea = fast_exp2(la - m2), eb = fast_exp2(lse_b - m2);
-            const float inv2 = 1.f / (ea + eb);
-            wa = ea * inv2;
-            wb = eb * inv2;
-            lse_new = m2 + fast_log2(ea + eb);
+          for (int j = 0; j < kMaxPieces; ++j) {
+            lp[j] = j == j_piece ? lse_own[g] : (j < n_pieces ? lp[j] : -INFINITY);
+            m = fmaxf(m, lp[j]);
           }
-        }
-        const size_t orow = lrow * D;
+          float esum = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < G::kDTiles; ++dt) {
-          // One 32-column tile of each other slot (slot i, or i + 1 from this
-          // piece's own on), loaded back to back.
-          f32x4 pv[kMaxPieces - 1][4];
+          for (int j = 0; j < kMaxPieces; ++j) {
+            wp[j] = j < n_pieces ? fast_exp2(lp[j] - m) : 0.f;
+            esum += wp[j];
+          }
+          const float einv = 1.f / esum;
 #pragma unroll
-          for (int i = 0; i < kMaxPieces - 1; ++i) {
-            if (i < n_pieces - 1) {  // workgroup-uniform
-#pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) {
-                const int d0 = dt * 32 + 8 * q4 + 4 * hi;
-                pv[i][q4] = d0 < D ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                   slot_rsrc(i + (i >= j_piece)), (row * D + d0) * 4, 0, kCoherent))
-                                   : f32x4{};
-              }
-            } else {
-#pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4) pv[i][q4] = f32x4{};
+          for (int j = 0; j < kMaxPieces; ++j) wp[j] *= einv;
+          const float lse_b = m + fast_log2(esum);
+          // Fold into the running (Out, LSE) as in the unsplit epilogue.
+          float wa = 0.f, wb = 1.f, lse_new = lse_b;
+          bool has_a = false;
+          if constexpr (MERGE) {
+            const float la = LSE[lrow] * kLog2e;
+            has_a = la != -INFINITY;
+            if (has_a) {
+              const float m2 = fmaxf(la, lse_b);
+              const float ea = fast_exp2(la - m2), eb = fast_exp2(lse_b - m2);
+              const float inv2 = 1.f / (ea + eb);
+              wa = ea * inv2;
+              wb = eb * inv2;
+              lse_new = m2 + fast_log2(ea + eb);
             }
           }
+          const size_t orow = lrow * D;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int d0 = dt * 32 + 8 * q4 + 4 * hi;
-            if (d0 < D) {
-              float o[4] = {0.f, 0.f, 0.f, 0.f};
+          for (int dt = 0; dt < G::kDTiles; ++dt) {
+            // One 32-column tile of each other slot (slot i, or i + 1 from this
+            // piece's own on), loaded back to back.
+            f32x4 pv[kMaxPieces - 1][4];
 #pragma unroll
-              for (int j = 0; j < kMaxPieces; ++j) {
+            for (int i = 0; i < kMaxPieces - 1; ++i) {
+              if (i < n_pieces - 1) {  // workgroup-uniform
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  // piece j: own below, else slot j (j < own) or loaded entry j - 1
-                  const float lo = j < kMaxPieces - 1 ? pv[j < kMaxPieces - 1 ? j : 0][q4][e] : 0.f;
-                  const float up = j > 0 ? pv[j > 0 ? j - 1 : 0][q4][e] : 0.f;
-                  const float pj = j == j_piece ? acc[g][dt][4 * q4 + e]
-                                                : (j >= n_pieces ? 0.f : (j < j_piece ? lo : up));
-                  o[e] = fmaf(wp[j], pj, o[e]);
+                for (int q4 = 0; q4 < 4; ++q4) {
+                  const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+                  pv[i][q4] = d0 < D
+                                  ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        slot_rsrc(i + (i >= j_piece)), (row * D + d0) * 4, 0, kCoherent))
+                                  : f32x4{};
                 }
-              }
-              if constexpr (OUT_F32) {
-                f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
-                if (MERGE && has_a) {
-                  const f32x4 a = *p;
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], wb * o[e]);
-                }
-                *p = f32x4{o[0], o[1], o[2], o[3]};
               } else {
-                bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
-                if (MERGE && has_a) {
-                  const bf16x4 a = *p;
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], wb * o[e]);
+                for (int q4 = 0; q4 < 4; ++q4) pv[i][q4] = f32x4{};
+              }
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+              if (d0 < D) {
+                float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < kMaxPieces; ++j) {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) {
+                    // piece j: own below, else slot j (j < own) or loaded entry j - 1
+                    const float lo = j < kMaxPieces - 1 ? pv[j < kMaxPieces - 1 ? j : 0][q4][e] : 0.f;
+                    const float up = j > 0 ? pv[j > 0 ? j - 1 : 0][q4][e] : 0.f;
+                    const float pj = j == j_piece ? acc[g][dt][4 * q4 + e]
+                                                  : (j >= n_pieces ? 0.f : (j < j_piece ? lo : up));
+                    o[e] = fmaf(wp[j], pj, o[e]);
+                  }
                 }
-                *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+                if constexpr (OUT_F32) {
+                  f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(Out) + orow + d0);
+                  if (MERGE && has_a) {
+                    const f32x4 a = *p;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, a[e], wb * o[e]);
+                  }
+                  *p = f32x4{o[0], o[1], o[2], o[3]};
+                } else {
+                  bf16x4* p = reinterpret_cast<bf16x4*>(static_cast<__bf16*>(Out) + orow + d0);
+                  if (MERGE && has_a) {
+                    const bf16x4 a = *p;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = fmaf(wa, (float)a[e], wb * o[e]);
+                  }
+                  *p = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+                }
               }
             }
           }
+          if (hi == 0) LSE[lrow] = lse_new * kLn2;
         }
-        if (hi == 0) LSE[lrow] = lse_new * kLn2;
       }
     }
-  }
-  if constexpr (SPLIT) __syncthreads();  // LDS is reused by the next piece
+    if constexpr (SPLIT) __syncthreads();  // LDS is reused by the next piece
   }  // piece loop
 }
 
@@ -871,18 +873,13 @@ hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, f
   using Kern = void (*)(const __bf16*, const __bf16*, const __bf16*, void*, float*, int, int, int,
                         float, int, unsigned*, float*);
   const bool split = split_grid > 0;
-  Kern kern;
-  if (out_f32) {
-    if (merge)
-      kern = split ? attn_fwd_bf16_kernel<D, NG, true, true, true> : attn_fwd_bf16_kernel<D, NG, true, true, false>;
-    else
-      kern = split ? attn_fwd_bf16_kernel<D, NG, true, false, true> : attn_fwd_bf16_kernel<D, NG, true, false, false>;
-  } else {
-    if (merge)
-      kern = split ? attn_fwd_bf16_kernel<D, NG, false, true, true> : attn_fwd_bf16_kernel<D, NG, false, true, false>;
-    else
-      kern = split ? attn_fwd_bf16_kernel<D, NG, false, false, true> : attn_fwd_bf16_kernel<D, NG, false, false, false>;
-  }
+  // [out_f32][merge][split]
+  static constexpr Kern kKernels[2][2][2] = {
+      {{attn_fwd_bf16_kernel<D, NG, false, false, false>, attn_fwd_bf16_kernel<D, NG, false, false, true>},
+       {attn_fwd_bf16_kernel<D, NG, false, true, false>, attn_fwd_bf16_kernel<D, NG, false, true, true>}},
+      {{attn_fwd_bf16_kernel<D, NG, true, false, false>, attn_fwd_bf16_kernel<D, NG, true, false, true>},
+       {attn_fwd_bf16_kernel<D, NG, true, true, false>, attn_fwd_bf16_kernel<D, NG, true, true, true>}}};
+  const Kern kern = kKernels[out_f32][merge][split];
   unsigned* ws_count = nullptr;
   float* ws_part = nullptr;
   if (split) {
