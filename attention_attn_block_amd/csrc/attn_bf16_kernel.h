@@ -6,9 +6,10 @@
 // parallel DiT device repeats per KV block ("SwiftFusion: Scalable Sequence
 // Parallelism for Distributed Inference of Diffusion Transformers on GPUs",
 // sections 1-2; "xDiT: an Inference Engine for Diffusion Transformers (DiTs)
-// with Massive Parallelism", abstract).  The key loop is the usual one-pass
-// online softmax: a running row maximum and normaliser, with the output
-// rescaled whenever the maximum grows, so each KV tile is read once.
+// with Massive Parallelism", abstract).  The key loop is a one-pass online
+// softmax: a reference row maximum and a running normaliser, with the output
+// rescaled only when a row's scores outgrow the reference by a fixed margin
+// (lazy rescaling, see kTau), so each KV tile is read once.
 //
 // Work decomposition (CDNA4, wave64):
 //  * A workgroup owns 256 query rows of one (batch, head); each of its eight
@@ -38,6 +39,12 @@
 //  * Workgroup ids are remapped so that all query tiles of a head run on the
 //    same XCD (ids are dealt round-robin over the 8 XCDs), sharing that XCD's
 //    L2 for the head's K/V stream.
+//  * Plain launch: one workgroup per query tile.  Split launch (SPLIT): a
+//    fixed grid shares the (query tile, key tile) units evenly, so a query
+//    tile's key range may be cut into pieces on different workgroups whose
+//    partials are combined through a caller workspace (see the kernel's
+//    SPLIT notes).  Each workgroup loops over its pieces with the same
+//    pipeline.
 // Scores are kept in the log2 domain (scale * log2 e folded into one FMA) and
 // exponentiated with v_exp_f32; the LSE is converted back to natural log.
 // P is rounded to bfloat16 (RNE, v_cvt_pk_bf16_f32) for the PV product and

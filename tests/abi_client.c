@@ -7,7 +7,8 @@
  *
  * in.bin  : int32 B, H, Nq, Nkv, d, nblocks; float32 scale;
  *           Q [B,H,Nq,d], K, V [B,H,Nkv,d] as bfloat16 bit patterns (uint16).
- * out.bin : for each of (full attention, unfused block fold, fused block fold):
+ * out.bin : for each of (full attention, unfused block fold, fused block fold,
+ *           full attention through attn_block_fwd_ws with a forced split):
  *           O [B,H,Nq,d] float32 then LSE [B,H,Nq] float32.
  * The KV rows are cut into `nblocks` consecutive blocks of near-equal length.
  * Exit status 0 on success; any failing call prints its status text.
@@ -66,7 +67,8 @@ int main(int argc, char** argv) {
   hipStream_t st;
   HIP_OK(hipStreamCreate(&st));
   void *dq, *dk, *dv, *dkb, *dvb;
-  float *o_full, *l_full, *o_acc, *l_acc, *o_tmp, *l_tmp, *o_fus, *l_fus;
+  float *o_full, *l_full, *o_acc, *l_acc, *o_tmp, *l_tmp, *o_fus, *l_fus, *o_ws, *l_ws;
+  void* ws;
   HIP_OK(hipMalloc(&dq, nq * 2));
   HIP_OK(hipMalloc(&dk, nkv * 2));
   HIP_OK(hipMalloc(&dv, nkv * 2));
@@ -80,6 +82,12 @@ int main(int argc, char** argv) {
   HIP_OK(hipMalloc((void**)&l_acc, BH * Nq * 4));
   HIP_OK(hipMalloc((void**)&l_tmp, BH * Nq * 4));
   HIP_OK(hipMalloc((void**)&l_fus, BH * Nq * 4));
+  HIP_OK(hipMalloc((void**)&o_ws, nq * 4));
+  HIP_OK(hipMalloc((void**)&l_ws, BH * Nq * 4));
+  const long long ws_bytes = attn_block_workspace_bytes(B, H, Nq, Nkv, d);
+  if (ws_bytes <= 0) return 2;
+  HIP_OK(hipMalloc(&ws, (size_t)ws_bytes));
+  HIP_OK(hipMemset(ws, 0, (size_t)ws_bytes)); /* counters start at zero */
   HIP_OK(hipMemcpy(dq, hq, nq * 2, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(dk, hk, nkv * 2, hipMemcpyHostToDevice));
   HIP_OK(hipMemcpy(dv, hv, nkv * 2, hipMemcpyHostToDevice));
@@ -87,6 +95,10 @@ int main(int argc, char** argv) {
   /* 1. full attention */
   DIT_OK_OR_FAIL(attn_block_fwd(dq, dk, dv, o_full, l_full, B, H, Nq, Nkv, d, scale, DIT_BF16,
                                 DIT_F32, st));
+
+  /* 4. the same through the workspace call (split where the grid allows) */
+  DIT_OK_OR_FAIL(attn_block_fwd_ws(dq, dk, dv, o_ws, l_ws, B, H, Nq, Nkv, d, scale, DIT_BF16,
+                                   DIT_F32, DIT_WS_FORCE_SPLIT, ws, ws_bytes, st));
 
   /* 2./3. block folds: copy each block into contiguous [B,H,n,d] buffers */
   float* ninf = (float*)malloc(BH * Nq * 4);
@@ -127,8 +139,8 @@ int main(int argc, char** argv) {
   if (!fo) return 2;
   float* ho = (float*)malloc(nq * 4);
   float* hl = (float*)malloc(BH * Nq * 4);
-  float* outs[3][2] = {{o_full, l_full}, {o_acc, l_acc}, {o_fus, l_fus}};
-  for (int r = 0; r < 3; ++r) {
+  float* outs[4][2] = {{o_full, l_full}, {o_acc, l_acc}, {o_fus, l_fus}, {o_ws, l_ws}};
+  for (int r = 0; r < 4; ++r) {
     HIP_OK(hipMemcpy(ho, outs[r][0], nq * 4, hipMemcpyDeviceToHost));
     HIP_OK(hipMemcpy(hl, outs[r][1], BH * Nq * 4, hipMemcpyDeviceToHost));
     if (fwrite(ho, 4, nq, fo) != nq || fwrite(hl, 4, BH * Nq, fo) != BH * Nq) return 2;

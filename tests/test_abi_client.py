@@ -2,7 +2,8 @@
 library): no Python binding in the loop.  The CPU tests check that the client
 links against libdit_attn.so and rejects bad input before any HIP call; the GPU
 test runs full attention and both block folds (separate merge, fused merge)
-through it and compares every output with the fp64 oracle."""
+through it, and full attention once more through the workspace call, and
+compares every output with the fp64 oracle."""
 
 import os
 import subprocess
@@ -42,7 +43,8 @@ def test_client_rejects_bad_input(tmp_path):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("shape", [(1, 3, 300, 777, 128, 3), (2, 2, 129, 200, 72, 2)])
+@pytest.mark.parametrize("shape", [(1, 3, 300, 777, 128, 3), (2, 2, 129, 200, 72, 2),
+                                   (1, 24, 2048, 700, 128, 2)])
 def test_c_client_matches_oracle(tmp_path, shape):
     B, H, Nq, Nkv, d, nb = shape
     print("case c-client", shape, flush=True)
@@ -60,9 +62,9 @@ def test_c_client_matches_oracle(tmp_path, shape):
     assert p.returncode == 0, p.stdout + p.stderr
     raw = np.fromfile(fout, np.float32)
     no, nl = B * H * Nq * d, B * H * Nq
-    assert raw.size == 3 * (no + nl)
+    assert raw.size == 4 * (no + nl)
     Or, Lr = oracle.ref_attn(qb, kb, vb, scale)
-    for r, what in enumerate(("full", "block fold", "fused block fold")):
+    for r, what in enumerate(("full", "block fold", "fused block fold", "workspace call")):
         o = raw[r * (no + nl): r * (no + nl) + no].reshape(B, H, Nq, d)
         l = raw[r * (no + nl) + no: (r + 1) * (no + nl)].reshape(B, H, Nq)
         assert_bf16_close(o.astype(np.float64), Or, f"c-client {what} O")
