@@ -34,10 +34,11 @@ def counters_zero(ws, B, H, Nq):
 
 
 # Shapes whose plain grid (one 256-row query tile per workgroup) leaves part of
-# a 256-CU GPU idle, so a forced split is taken; the last three are ragged in
-# query rows, keys or both, and cut some query tiles into three pieces.
+# a 256-CU GPU idle, so a forced split is taken.  Pieces per query tile on 256
+# CUs: 2 for the first two; 2 or 3 for the next two; 3 or 4 for the last two.
+# All but the first are ragged in query rows, keys or both.
 SPLIT_SHAPES = [(1, 24, 2048, 2048, 128), (1, 24, 2000, 700, 128), (3, 10, 1111, 517, 72),
-                (1, 150, 256, 333, 64)]
+                (1, 150, 256, 333, 64), (2, 50, 200, 620, 128), (1, 90, 250, 700, 72)]
 
 
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
