@@ -218,18 +218,32 @@ __global__ __launch_bounds__(kThreads) void cfg_relmae_kernel(const float* u, co
   const float t = 1.f - s;
   float num = 0.f, den = 0.f;
   const long long base = (long long)blockIdx.x * kRelmaeGroupsPerBlock + threadIdx.x;
+  // All of the lane's loads first: `out` may be `u` or `c` itself, and the
+  // compiler cannot move a load above an earlier store that might alias it,
+  // so a load-compute-store loop would make one HBM round trip per group.
+  // Aliasing is only ever exact (same index), so each group's store still
+  // follows its own loads.
+  constexpr int kG = kRelmaeGroupsPerBlock / kThreads;
+  f32x4 a[kG], b[kG];
 #pragma unroll
-  for (int k = 0; k < kRelmaeGroupsPerBlock / kThreads; ++k) {
+  for (int k = 0; k < kG; ++k) {
     const long long i = base + (long long)k * kThreads;
     if (i < n4) {
-      const f32x4 a = __builtin_nontemporal_load(u4 + i), b = __builtin_nontemporal_load(c4 + i);
+      a[k] = __builtin_nontemporal_load(u4 + i);
+      b[k] = __builtin_nontemporal_load(c4 + i);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kG; ++k) {
+    const long long i = base + (long long)k * kThreads;
+    if (i < n4) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        num += fabsf(b[e] - a[e]);
-        den += fabsf(a[e]);
+        num += fabsf(b[k][e] - a[k][e]);
+        den += fabsf(a[k][e]);
       }
-      __builtin_nontemporal_store(f32x4{fmaf(s, b[0], t * a[0]), fmaf(s, b[1], t * a[1]),
-                                        fmaf(s, b[2], t * a[2]), fmaf(s, b[3], t * a[3])},
+      __builtin_nontemporal_store(f32x4{fmaf(s, b[k][0], t * a[k][0]), fmaf(s, b[k][1], t * a[k][1]),
+                                        fmaf(s, b[k][2], t * a[k][2]), fmaf(s, b[k][3], t * a[k][3])},
                                   o4 + i);
     }
   }
@@ -258,13 +272,30 @@ __global__ __launch_bounds__(kThreads) void cfg_relmae_kernel(const float* u, co
   }
 }
 
-__global__ __launch_bounds__(kThreads) void relmae_finish_kernel(const float* work, int nblk,
-                                                                float* relmae) {
-  __shared__ double red[2][kThreads / 64];
+constexpr int kFinishThreads = 1024;  // one workgroup: as many loads in flight as it can hold
+
+__global__ __launch_bounds__(kFinishThreads) void relmae_finish_kernel(const float* work, int nblk,
+                                                                      float* relmae) {
+  __shared__ double red[2][kFinishThreads / 64];
   double num = 0.0, den = 0.0;
-  for (int i = threadIdx.x; i < nblk; i += kThreads) {
-    num += work[2 * i];
-    den += work[2 * i + 1];
+  // Lane t adds entries t, t + kFinishThreads, ... in that order;
+  // eight (num, den) pairs are loaded before they are added, and entries past
+  // the end add +0, so the order (and the result) is fixed.
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2* w2 = reinterpret_cast<const f32x2*>(work);
+  constexpr int kU = 8;
+  for (int i0 = threadIdx.x; i0 < nblk; i0 += kFinishThreads * kU) {
+    f32x2 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * kFinishThreads;
+      v[u] = i < nblk ? w2[i] : f32x2{0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      num += v[u][0];
+      den += v[u][1];
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -278,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void relmae_finish_kernel(const float* wo
   __syncthreads();
   if (threadIdx.x == 0) {
     double a = 0.0, b = 0.0;
-    for (int w = 0; w < kThreads / 64; ++w) {
+    for (int w = 0; w < kFinishThreads / 64; ++w) {
       a += red[0][w];
       b += red[1][w];
     }
@@ -357,7 +388,7 @@ hipError_t launch_cfg_relmae(const float* u, const float* c, float* out, long lo
   const long long blocks = cfg_relmae_work_floats(n) / 2;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   cfg_relmae_kernel<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(u, c, out, n, s, work);
-  relmae_finish_kernel<<<dim3(1), kThreads, 0, stream>>>(work, (int)blocks, relmae);
+  relmae_finish_kernel<<<dim3(1), kFinishThreads, 0, stream>>>(work, (int)blocks, relmae);
   return hipGetLastError();
 }
 
