@@ -17,7 +17,11 @@ Prints ONE JSON line.  `value` is attention TFLOP/s over the whole step
 merges, splice and CFG included).  Per-phase times, the roofline of the
 dominant kernel and the fp64 CPU oracle on a bounded sample ride along.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 200] [--no-cpu-baseline]
+
+The default warm-up (about 0.7 s of steps) lets the shader clock settle at its
+steady value under this load before timing; the clock and board power sampled
+during the timed steps are reported (clock_during_timed_steps).
 """
 
 import argparse
@@ -43,7 +47,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-supplementary", action="store_true")
     return ap.parse_args()
@@ -180,11 +184,14 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    sampler = ClockSampler()
+    sampler.start()
     t_start.record()
     for k in range(args.steps):
         step(evs[k])
     t_end.record()
     torch.cuda.synchronize()
+    clock = sampler.stop()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
     ring_ms, merge_ms, patch_ms, cfg_ms = [], [], [], []
@@ -245,11 +252,72 @@ def main():
                    "attn_flops_per_step": f_step, "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
         "roofline": roofline,
         "phases": phases,
+        "clock_during_timed_steps": clock,
         "supplementary": supp,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wp)
     print(json.dumps(out), flush=True)
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (pp_dpm_sclk, the level marked
+    '*') and board power (hwmon power1_input) from sysfs every 20 ms on a
+    background thread, for the timed region only.  Reports null where the
+    files do not exist."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.samples = []
+        self.path = None
+        for dev_dir in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if os.path.exists(os.path.join(dev_dir, "pp_dpm_sclk")):
+                self.path = dev_dir
+                break
+        self.power = None
+        if self.path:
+            hw = sorted(glob.glob(os.path.join(self.path, "hwmon", "*", "power1_input")))
+            self.power = hw[0] if hw else None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        with open(os.path.join(self.path, "pp_dpm_sclk")) as f:
+            m = re.search(r"(\d+)\s*Mhz\s*\*", f.read())
+        w = None
+        if self.power:
+            with open(self.power) as f:
+                w = int(f.read().strip()) / 1e6
+        return (int(m.group(1)) if m else None, w)
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except (OSError, ValueError):
+                return
+            time.sleep(0.02)
+
+    def start(self):
+        if self.path:
+            self._thread.start()
+
+    def stop(self):
+        if not self.path:
+            return None
+        self._stop.set()
+        self._thread.join()
+        clk = sorted(c for c, _ in self.samples if c)
+        pw = sorted(w for _, w in self.samples if w is not None)
+        if not clk:
+            return None
+
+        def q(a, f):
+            return a[int(f * (len(a) - 1))] if a else None
+        return {"sclk_mhz_median": q(clk, 0.5), "sclk_mhz_p10": q(clk, 0.1),
+                "sclk_mhz_p90": q(clk, 0.9), "power_w_median": q(pw, 0.5),
+                "samples": len(clk), "source": "sysfs pp_dpm_sclk / hwmon power1_input, 20 ms"}
 
 
 def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):
