@@ -406,6 +406,28 @@ def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):
     res["long_block_160_tiles"] = row
     del q, k, v, out, lse, wsp
 
+    # Ulysses share of the video workload on 8 devices: H/8 = 3 heads against
+    # the full 32768-token sequence (384 query tiles: 1.5 waves of workgroups
+    # on 256 CUs), bf16 out, plain grid vs split launch.
+    shp = (1, 3, 32768, 32768, 128)
+    q = torch.randn(shp[0], shp[1], shp[2], shp[4], device=dev, generator=g).to(torch.bfloat16)
+    k = torch.randn(shp[0], shp[1], shp[3], shp[4], device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn(shp[0], shp[1], shp[3], shp[4], device=dev, generator=g).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    wsp = attn_block_workspace(q, k)
+    f = attn_flops(shp[0], shp[1], shp[2], shp[3], shp[4])
+    row = {"shape_b_h_nq_nkv_d": list(shp)}
+    for tag, kw in (("plain", {}), ("split", {"workspace": wsp})):
+        fn = lambda i: attn_block_fwd(q, k, v, out=out, lse=lse, **kw)
+        for i in range(5):
+            fn(i)
+        us = timed(fn, 10)
+        row[f"{tag}_us"] = us
+        row[f"{tag}_tflops"] = f / (us * 1e-6) / 1e12
+    res["ulysses_share_video_p8"] = row
+    del q, k, v, out, lse, wsp
+
     # d = 72 attention: PixArt-style 1024 px and DiT-XL/2 256 px.
     for name in ("pixart_1024", "dit_xl_256"):
         w = inputs.make(name)

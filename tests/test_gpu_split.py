@@ -112,6 +112,28 @@ def test_long_block_splits_by_default_sampled_rows(out_dtype):
     assert_bf16_close(to_f64(L[:, :, rows]), Lr, "long split LSE (sampled rows)")
 
 
+def test_ulysses_share_video_split_sampled_rows():
+    """A Ulysses share of the video workload on 8 devices (3 heads x 32768
+    queries x 32768 keys, d128): 384 query tiles, split by default; sampled
+    rows of every head against the oracle."""
+    B, H, N, d = 1, 3, 32768, 128
+    q, k, v = inputs.attn_inputs(B, H, N, N, d, "bf16", seed=23)
+    scale = inputs.default_scale(d)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    say("case ulysses share split")
+    ws = attn_block_workspace(qd, kd)
+    O, L = attn_block_fwd(qd, kd, vd, scale=scale, workspace=ws)
+    Op, Lp = attn_block_fwd(qd, kd, vd, scale=scale)
+    torch.cuda.synchronize()
+    assert counters_zero(ws, B, H, N)
+    assert not (torch.equal(O, Op) and torch.equal(L, Lp)), "split launch was not taken"
+    rng = np.random.default_rng(24)
+    rows = np.unique(np.concatenate([[0, 255, 256, N - 1], rng.choice(N, 40, replace=False)]))
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale, rows=rows)
+    assert_bf16_close(to_f64(O[:, :, rows]), Or, "ulysses split O (sampled rows)")
+    assert_bf16_close(to_f64(L[:, :, rows]), Lr, "ulysses split LSE (sampled rows)")
+
+
 @pytest.mark.parametrize("acc_dtype", [torch.float32, torch.bfloat16])
 def test_ring_2048px_split_fused(acc_dtype):
     """The ring share (8 KV blocks of 2048 keys, 24 heads, 2048 queries) with
