@@ -18,7 +18,7 @@ DIT_OK, DIT_ERR_INVALID_ARG, DIT_ERR_UNSUPPORTED, DIT_ERR_HIP = 0, 1, 2, 3
 DIT_F32, DIT_BF16 = 0, 1
 
 EXPORTS = ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws",
-           "attn_block_workspace_bytes", "attn_lse_merge", "attn_patch_fwd",
+           "attn_block_workspace_bytes", "attn_lse_merge", "attn_patch_fwd", "attn_patch_fwd_ws",
            "cfg_combine", "cfg_combine_relmae", "cfg_combine_relmae_workspace",
            "dit_status_string")
 
@@ -49,12 +49,14 @@ def load():
     L.attn_block_workspace_bytes.restype = ll
     L.attn_lse_merge.argtypes = [vp, vp, vp, vp, ll, i, i, vp]
     L.attn_patch_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    L.attn_patch_fwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, ll,
+                                    vp]
     L.cfg_combine.argtypes = [vp, vp, vp, ll, f, vp]
     L.cfg_combine_relmae.argtypes = [vp, vp, vp, ll, f, vp, vp, vp]
     L.cfg_combine_relmae_workspace.argtypes = [ll]
     L.cfg_combine_relmae_workspace.restype = ll
     for name in ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws", "attn_lse_merge",
-                 "attn_patch_fwd", "cfg_combine", "cfg_combine_relmae"):
+                 "attn_patch_fwd", "attn_patch_fwd_ws", "cfg_combine", "cfg_combine_relmae"):
         getattr(L, name).restype = ctypes.c_int
     L.dit_status_string.argtypes = [ctypes.c_int]
     L.dit_status_string.restype = ctypes.c_char_p
@@ -201,9 +203,11 @@ def attn_lse_merge(o_a, lse_a, o_b, lse_b):
 
 
 def attn_patch_fwd(q_p, k_p, v_p, k_buf, v_buf, p0, scale=None, out_dtype=None, out=None,
-                   lse=None):
+                   lse=None, workspace=None):
     """Splice k_p/v_p into rows [p0, p0+Np) of k_buf/v_buf (in place), then
-    attend q_p to the whole buffer.  Returns (O, LSE)."""
+    attend q_p to the whole buffer.  Returns (O, LSE).  With a workspace
+    (attn_block_workspace(q_p, k_buf)) the attention may take the split
+    launch (attn_patch_fwd_ws)."""
     dev = _dev(q_p, k_p, v_p, k_buf, v_buf)
     B, H, Np, d = q_p.shape
     N = k_buf.shape[2]
@@ -220,6 +224,18 @@ def attn_patch_fwd(q_p, k_p, v_p, k_buf, v_buf, p0, scale=None, out_dtype=None, 
     _dev(q_p, out, lse)
     if out.shape != (B, H, Np, d) or out.dtype != out_dtype or lse.shape != (B, H, Np):
         raise ValueError("out/lse shape or dtype mismatch")
+    if workspace is not None:
+        _dev(q_p, workspace)
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor (attn_block_workspace)")
+        with torch.cuda.device(dev):
+            rc = load().attn_patch_fwd_ws(q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(),
+                                          k_buf.data_ptr(), v_buf.data_ptr(), out.data_ptr(),
+                                          lse.data_ptr(), B, H, Np, N, int(p0), d, scale,
+                                          _dtype(q_p.dtype), _dtype(out_dtype),
+                                          workspace.data_ptr(), workspace.numel(), _stream(dev))
+        _check("attn_patch_fwd_ws", rc)
+        return out, lse
     with torch.cuda.device(dev):
         rc = load().attn_patch_fwd(q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(),
                                    k_buf.data_ptr(), v_buf.data_ptr(), out.data_ptr(),

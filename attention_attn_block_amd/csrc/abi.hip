@@ -73,6 +73,12 @@ dit_status_t run_attn(const void* Q, const void* K, const void* V, void* O, floa
                                        BH, Nq, Nkv, d, scale, merge, stream));
 }
 
+// attn_patch_fwd with an optional split workspace (null: plain launch).
+dit_status_t patch_fwd(const void* Q_p, const void* K_p, const void* V_p, void* K_buf, void* V_buf,
+                       void* O, float* LSE, int B, int H, int Np, int N, int p0, int d, float scale,
+                       dit_dtype_t in_dtype, dit_dtype_t out_dtype, void* ws, long long ws_bytes,
+                       hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -158,6 +164,27 @@ dit_status_t attn_patch_fwd(const void* Q_p, const void* K_p, const void* V_p, v
                             void* V_buf, void* O, float* LSE, int B, int H, int Np, int N, int p0,
                             int d, float scale, dit_dtype_t in_dtype, dit_dtype_t out_dtype,
                             hipStream_t stream) {
+  return patch_fwd(Q_p, K_p, V_p, K_buf, V_buf, O, LSE, B, H, Np, N, p0, d, scale, in_dtype,
+                   out_dtype, nullptr, 0, stream);
+}
+
+dit_status_t attn_patch_fwd_ws(const void* Q_p, const void* K_p, const void* V_p, void* K_buf,
+                               void* V_buf, void* O, float* LSE, int B, int H, int Np, int N,
+                               int p0, int d, float scale, dit_dtype_t in_dtype,
+                               dit_dtype_t out_dtype, void* workspace, long long workspace_bytes,
+                               hipStream_t stream) {
+  if (!workspace) return DIT_ERR_INVALID_ARG;
+  return patch_fwd(Q_p, K_p, V_p, K_buf, V_buf, O, LSE, B, H, Np, N, p0, d, scale, in_dtype,
+                   out_dtype, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+dit_status_t patch_fwd(const void* Q_p, const void* K_p, const void* V_p, void* K_buf, void* V_buf,
+                       void* O, float* LSE, int B, int H, int Np, int N, int p0, int d, float scale,
+                       dit_dtype_t in_dtype, dit_dtype_t out_dtype, void* ws, long long ws_bytes,
+                       hipStream_t stream) {
   if (!K_p || !V_p || !K_buf || !V_buf) return DIT_ERR_INVALID_ARG;
   if (N <= 0 || Np <= 0 || p0 < 0 || (long long)p0 + Np > N) return DIT_ERR_INVALID_ARG;
   size_t qb, kvb, ob, lb;
@@ -175,14 +202,25 @@ dit_status_t attn_patch_fwd(const void* Q_p, const void* K_p, const void* V_p, v
   const void* ins[5] = {Q_p, K_p, V_p, K_buf, V_buf};
   const size_t inb[5] = {pb, pb, pb, kvb, kvb};
   if (outputs_clash(O, ob, LSE, lb, ins, inb, 5)) return DIT_ERR_INVALID_ARG;
+  if (ws) {
+    const long long need = attn_block_workspace_bytes(B, H, Np, N, d);
+    if (ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u)) return DIT_ERR_INVALID_ARG;
+    const void* all[7] = {Q_p, K_p, V_p, K_buf, V_buf, O, LSE};
+    const size_t allb[7] = {pb, pb, pb, kvb, kvb, ob, lb};
+    for (int i = 0; i < 7; ++i)
+      if (overlaps(ws, (size_t)need, all[i], allb[i])) return DIT_ERR_INVALID_ARG;
+  }
 
   const long long row_units = (long long)d * (long long)elt_size(in_dtype) / 16;
   hipError_t e = dit::launch_splice2(K_p, K_buf, V_p, V_buf, B * H, (long long)Np * row_units,
                                      (long long)N * row_units, (long long)p0 * row_units, stream);
   if (e != hipSuccess) return DIT_ERR_HIP;
   return run_attn(Q_p, K_buf, V_buf, O, LSE, B * H, Np, N, d, scale, in_dtype, out_dtype, false,
-                  nullptr, false, stream);
+                  ws, false, stream);
 }
+}  // namespace
+
+extern "C" {
 
 dit_status_t cfg_combine(const float* eps_u, const float* eps_c, float* out, long long n, float s,
                          hipStream_t stream) {

@@ -326,7 +326,8 @@ def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):
     with few query tiles (plain grid vs split launch), and the d=72
     workloads."""
     from attention_attn_block_amd import (attn_block_fwd, attn_block_fwd_merge, attn_block_workspace,
-                                          attn_lse_merge, cfg_combine, cfg_combine_relmae)
+                                          attn_lse_merge, attn_patch_fwd, cfg_combine,
+                                          cfg_combine_relmae)
     res = {}
 
     def timed(fn, iters):
@@ -427,6 +428,29 @@ def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):
         row[f"{tag}_tflops"] = f / (us * 1e-6) / 1e12
     res["ulysses_share_video_p8"] = row
     del q, k, v, out, lse, wsp
+
+    # PipeFusion on 8 devices over the same 32768-token sequence: a 4096-query
+    # patch (24 heads: 384 query tiles, 1.5 waves) spliced at p0 = 8192 and
+    # attended to the whole buffer, plain grid vs split launch.
+    vp_ = inputs.video_patch(Np=4096)
+    q_p, k_p, v_p = (vp_[n].to(dev) for n in ("q_p", "k_p", "v_p"))
+    k_buf, v_buf = vp_["k_buf"].to(dev), vp_["v_buf"].to(dev)
+    out = torch.empty_like(q_p)
+    lse = torch.empty(q_p.shape[:3], dtype=torch.float32, device=dev)
+    wsp = attn_block_workspace(q_p, k_buf)
+    B, H, Np, dd = q_p.shape
+    f = attn_flops(B, H, Np, k_buf.shape[2], dd)
+    row = {"shape_b_h_np_n_d": [B, H, Np, k_buf.shape[2], dd], "p0": vp_["p0"]}
+    for tag, kw in (("plain", {}), ("split", {"workspace": wsp})):
+        fn = lambda i: attn_patch_fwd(q_p, k_p, v_p, k_buf, v_buf, vp_["p0"], scale=vp_["scale"],
+                                      out=out, lse=lse, **kw)
+        for i in range(5):
+            fn(i)
+        us = timed(fn, 10)
+        row[f"{tag}_us"] = us
+        row[f"{tag}_tflops"] = f / (us * 1e-6) / 1e12
+    res["pipefusion_patch_video_p8"] = row
+    del q_p, k_p, v_p, k_buf, v_buf, out, lse, wsp, vp_
 
     # d = 72 attention: PixArt-style 1024 px and DiT-XL/2 256 px.
     for name in ("pixart_1024", "dit_xl_256"):

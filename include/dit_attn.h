@@ -195,6 +195,27 @@ dit_status_t attn_patch_fwd(const void* Q_p, const void* K_p, const void* V_p,
                             hipStream_t stream);
 
 /*
+ * attn_patch_fwd with a split workspace (as attn_block_fwd_ws without flags):
+ * the attention over the buffer may share its query tiles' keys between
+ * workgroups.  A patch whose query tiles fill part of a wave of workgroups
+ * gains from it (for example 24 heads x 4096 patch queries, PipeFusion on 8
+ * devices over 32768 tokens: 384 tiles of 256 rows, 1.5 waves on 256
+ * compute units).  Patches of unequal size (Orchestra, abstract) make such
+ * fractions common.
+ *   workspace: at least attn_block_workspace_bytes(B, H, Np, N, d) bytes,
+ *              256-byte aligned, zero-filled before its first use, owned by
+ *              the caller, overlapping no tensor; one call at a time.
+ * Otherwise as attn_patch_fwd.
+ */
+dit_status_t attn_patch_fwd_ws(const void* Q_p, const void* K_p, const void* V_p,
+                               void* K_buf, void* V_buf,
+                               void* O, float* LSE,
+                               int B, int H, int Np, int N, int p0, int d, float scale,
+                               dit_dtype_t in_dtype, dit_dtype_t out_dtype,
+                               void* workspace, long long workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * Classifier-free guidance combine of the unconditional and conditional
  * noise predictions (Hybridiff, Technische Zusammenfassung, 2.A):
  *   out[i] = eps_u[i] + s * (eps_c[i] - eps_u[i]),

@@ -237,6 +237,28 @@ def test_attn_block_fwd_ws_rejects(lib, kw, code):
     assert block_ws(lib, **kw) == code
 
 
+def patch_ws(lib, **kw):
+    a = dict(Qp=ptr(0), Kp=ptr(1), Vp=ptr(2), Kb=ptr(3), Vb=ptr(4), O=ptr(5), LSE=ptr(6), B=1, H=24,
+             Np=4096, N=32768, p0=8192, d=128, scale=0.088, i=BF16, o=BF16, W=ptr(7), nbytes=None)
+    a.update(kw)
+    n = split_ws_bytes(a["B"], a["H"], a["Np"], a["d"]) if a["nbytes"] is None else a["nbytes"]
+    return lib.attn_patch_fwd_ws(a["Qp"], a["Kp"], a["Vp"], a["Kb"], a["Vb"], a["O"], a["LSE"],
+                                 a["B"], a["H"], a["Np"], a["N"], a["p0"], a["d"], a["scale"],
+                                 a["i"], a["o"], a["W"], n, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), INV),
+    (dict(nbytes=split_ws_bytes(1, 24, 4096, 128) - 4), INV),  # short
+    (dict(W=ptr(7, 128)), INV),                                  # not 256-byte aligned
+    (dict(W=ptr(3, 4096)), INV),                                 # inside K_buf
+    (dict(p0=30000), INV),                                       # patch past the buffer end
+    (dict(Kp=None), INV), (dict(d=100), UNS),
+])
+def test_attn_patch_fwd_ws_rejects(lib, kw, code):
+    assert patch_ws(lib, **kw) == code
+
+
 # ---------------------------------------------------------------------------
 # cfg_combine_relmae
 # ---------------------------------------------------------------------------

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from attention_attn_block_amd import (attn_block_fwd, attn_block_fwd_merge, attn_block_workspace,
-                                      inputs)
+                                      attn_patch_fwd, inputs)
 from attention_attn_block_amd.binding import load
 from tests.gpu_util import assert_bf16_close, to_f64, to_oracle
 
@@ -132,6 +132,33 @@ def test_ulysses_share_video_split_sampled_rows():
     Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale, rows=rows)
     assert_bf16_close(to_f64(O[:, :, rows]), Or, "ulysses split O (sampled rows)")
     assert_bf16_close(to_f64(L[:, :, rows]), Lr, "ulysses split LSE (sampled rows)")
+
+
+def test_pipefusion_patch_p8_split_sampled_rows():
+    """PipeFusion on 8 devices over the 32768-token video workload: a 4096-query
+    patch at p0 = 8192 (24 heads: 384 query tiles), through attn_patch_fwd_ws.
+    The spliced buffer bit for bit, sampled rows against the oracle, and the
+    split taken (its bits differ from the plain call's)."""
+    w = inputs.video_patch(Np=4096)
+    p0, Np = w["p0"], 4096
+    say("case pipefusion patch p8 split", tuple(w["k_buf"].shape))
+    qp, kp, vp = dev(w["q_p"]), dev(w["k_p"]), dev(w["v_p"])
+    kb, vb = dev(w["k_buf"]), dev(w["v_buf"])
+    ws = attn_block_workspace(qp, kb)
+    O, L = attn_patch_fwd(qp, kp, vp, kb, vb, p0, scale=w["scale"], workspace=ws)
+    Op, Lp = attn_patch_fwd(qp, kp, vp, kb, vb, p0, scale=w["scale"])   # splice again: same rows
+    torch.cuda.synchronize()
+    assert counters_zero(ws, 1, 24, Np)
+    assert not (torch.equal(O, Op) and torch.equal(L, Lp)), "split launch was not taken"
+    assert torch.equal(kb[:, :, p0:p0 + Np], kp) and torch.equal(vb[:, :, p0:p0 + Np], vp)
+    rng = np.random.default_rng(25)
+    rows = np.unique(np.concatenate([[0, 255, 256, Np - 1], rng.choice(Np, 40, replace=False)]))
+    Or, Lr, Kn, _ = oracle.ref_patch(to_oracle(w["q_p"]), to_oracle(w["k_p"]), to_oracle(w["v_p"]),
+                                     to_oracle(w["k_buf"]), to_oracle(w["v_buf"]), p0, w["scale"],
+                                     rows=rows)
+    assert np.array_equal(to_oracle(kb.cpu()), Kn), "spliced K buffer differs from the oracle's"
+    assert_bf16_close(to_f64(O[:, :, rows]), Or, "patch p8 split O (sampled rows)")
+    assert_bf16_close(to_f64(L[:, :, rows]), Lr, "patch p8 split LSE (sampled rows)")
 
 
 @pytest.mark.parametrize("acc_dtype", [torch.float32, torch.bfloat16])
