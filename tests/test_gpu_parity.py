@@ -188,6 +188,18 @@ def test_edge_shapes(shape, in_dtype, out_dtype):
     check_attn(q, k, v, inputs.default_scale(d), out_dtype, f"edge {shape}")
 
 
+ALL_HEAD_DIMS = list(range(8, 129, 8))
+
+
+@pytest.mark.parametrize("d", ALL_HEAD_DIMS)
+def test_every_head_dim(d):
+    """Every instantiated head dim on a ragged shape (query and key counts not
+    multiples of the tiles), bf16 in, bf16 and fp32 out."""
+    for out_dtype in (torch.bfloat16, torch.float32):
+        q, k, v = inputs.attn_inputs(1, 2, 300, 200, d, "bf16", seed=100 + d)
+        check_attn(q, k, v, inputs.default_scale(d), out_dtype, f"head dim {d}")
+
+
 def test_large_scores_stay_finite():
     """Scores of several hundred (peaked softmax) must not overflow."""
     q, k, v = inputs.attn_inputs(1, 2, 100, 300, 64, "bf16", seed=7)

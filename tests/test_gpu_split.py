@@ -65,6 +65,26 @@ def test_split_block_matches_oracle(shape, out_dtype):
     assert_bf16_close(to_f64(L), Lr, "split LSE")
 
 
+@pytest.mark.parametrize("d", list(range(8, 129, 8)))
+def test_forced_split_every_head_dim(d):
+    """The split kernels of every head dim: 150 heads x 256 queries x 333 keys
+    (150 query tiles, 6 ragged key tiles each, cut into 2 or 3 pieces)."""
+    B, H, Nq, Nkv = 1, 150, 256, 333
+    q, k, v = inputs.attn_inputs(B, H, Nq, Nkv, d, "bf16", seed=200 + d)
+    scale = inputs.default_scale(d)
+    say("case forced split head dim", d)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    ws = attn_block_workspace(qd, kd)
+    O, L = attn_block_fwd(qd, kd, vd, scale=scale, workspace=ws, force_split=True)
+    Op, Lp = attn_block_fwd(qd, kd, vd, scale=scale)
+    torch.cuda.synchronize()
+    assert counters_zero(ws, B, H, Nq)
+    assert not (torch.equal(O, Op) and torch.equal(L, Lp)), "split launch was not taken"
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale)
+    assert_bf16_close(to_f64(O), Or, f"split d{d} O")
+    assert_bf16_close(to_f64(L), Lr, f"split d{d} LSE")
+
+
 def test_plain_grid_shape_runs_unsplit():
     """768 query tiles fill three waves of 256 CUs: the workspace call takes
     the plain path and matches attn_block_fwd bit for bit."""
