@@ -194,10 +194,26 @@ ALL_HEAD_DIMS = list(range(8, 129, 8))
 @pytest.mark.parametrize("d", ALL_HEAD_DIMS)
 def test_every_head_dim(d):
     """Every instantiated head dim on a ragged shape (query and key counts not
-    multiples of the tiles), bf16 in, bf16 and fp32 out."""
+    multiples of the tiles): bf16 in with bf16 and fp32 out, fp32 in; and two
+    KV blocks folded by the fused merge into fp32 and bf16 accumulators."""
+    scale = inputs.default_scale(d)
     for out_dtype in (torch.bfloat16, torch.float32):
         q, k, v = inputs.attn_inputs(1, 2, 300, 200, d, "bf16", seed=100 + d)
-        check_attn(q, k, v, inputs.default_scale(d), out_dtype, f"head dim {d}")
+        check_attn(q, k, v, scale, out_dtype, f"head dim {d}")
+    q, k, v = inputs.attn_inputs(1, 2, 130, 90, d, "f32", seed=300 + d)
+    check_attn(q, k, v, scale, torch.float32, f"head dim {d} fp32")
+    q, k, v = inputs.attn_inputs(1, 2, 300, 200, d, "bf16", seed=400 + d)
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale)
+    for acc_dtype in (torch.float32, torch.bfloat16):
+        say("case fused merge head dim", d, acc_dtype)
+        o_acc = torch.full((1, 2, 300, d), float("nan"), dtype=acc_dtype, device="cuda:0")
+        l_acc = torch.full((1, 2, 300), -float("inf"), device="cuda:0")
+        for a, b in ((0, 77), (77, 200)):
+            attn_block_fwd_merge(dev(q), dev(k[:, :, a:b].contiguous()), dev(v[:, :, a:b].contiguous()),
+                                 o_acc, l_acc, scale=scale)
+        torch.cuda.synchronize()
+        assert_bf16_close(to_f64(o_acc), Or, f"fused d{d} O")
+        assert_bf16_close(to_f64(l_acc), Lr, f"fused d{d} LSE")
 
 
 def test_large_scores_stay_finite():
