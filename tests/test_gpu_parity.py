@@ -277,6 +277,43 @@ def test_merge_edge_cases():
         assert np.array_equal(to_oracle(ga.cpu())[keep], to_oracle(Oa)[keep])
 
 
+@pytest.mark.parametrize("d", list(range(8, 129, 8)))
+def test_merge_and_patch_every_head_dim(d):
+    """The merge (fp32 and bf16 partials, with empty rows) and the patch step
+    (splice bit for bit, then attention) at every supported head dim."""
+    rows = 300
+    g = torch.Generator().manual_seed(500 + d)
+    for dt in (torch.float32, torch.bfloat16):
+        Oa = torch.randn(rows, d, generator=g).to(dt)
+        Ob = torch.randn(rows, d, generator=g).to(dt)
+        La = torch.randn(rows, generator=g) * 3
+        Lb = torch.randn(rows, generator=g) * 3
+        La[::7] = -torch.inf
+        Lb[::5] = -torch.inf
+        ga, gla = dev(Oa), dev(La)
+        attn_lse_merge(ga, gla, dev(Ob), dev(Lb))
+        torch.cuda.synchronize()
+        Or, Lr = oracle.ref_lse_merge(to_oracle(Oa), to_oracle(La), to_oracle(Ob), to_oracle(Lb))
+        fin = ~np.isneginf(Lr)
+        assert np.array_equal(np.isneginf(to_f64(gla)), ~fin)
+        close = assert_f32_close if dt == torch.float32 else assert_bf16_close
+        close(to_f64(ga)[fin], Or[fin], f"merge d{d} O")
+        close(to_f64(gla)[fin], Lr[fin], f"merge d{d} LSE")
+    # patch: 70 fresh rows spliced at row 100 of a 260-row buffer
+    q_p, k_p, v_p = inputs.attn_inputs(1, 2, 70, 70, d, "bf16", seed=600 + d)
+    _, k_buf, v_buf = inputs.attn_inputs(1, 2, 1, 260, d, "bf16", seed=700 + d)
+    scale = inputs.default_scale(d)
+    kb, vb = dev(k_buf), dev(v_buf)
+    say("case patch head dim", d)
+    O, L = attn_patch_fwd(dev(q_p), dev(k_p), dev(v_p), kb, vb, 100, scale=scale)
+    torch.cuda.synchronize()
+    Or, Lr, Kn, Vn = oracle.ref_patch(to_oracle(q_p), to_oracle(k_p), to_oracle(v_p),
+                                      to_oracle(k_buf), to_oracle(v_buf), 100, scale)
+    assert np.array_equal(to_oracle(kb.cpu()), Kn) and np.array_equal(to_oracle(vb.cpu()), Vn)
+    assert_bf16_close(to_f64(O), Or, f"patch d{d} O")
+    assert_bf16_close(to_f64(L), Lr, f"patch d{d} LSE")
+
+
 def test_merge_in_place_alias():
     """b == a exactly: O unchanged (to rounding), LSE + ln 2."""
     g = torch.Generator().manual_seed(10)
