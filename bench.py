@@ -150,7 +150,11 @@ def main():
 
     n_ev = 2 * nblk + 2 * (nblk - 1) + 4
 
-    def step(ev=None):
+    def step(ev=None, patch_ev=None):
+        """One step.  `ev` (n_ev events) brackets every call, for the phase
+        breakdown; `patch_ev` (2 events) brackets only the patch call, for the
+        roofline.  The timed steps carry patch_ev only: an event between every
+        pair of kernels costs about 4% of the step."""
         i = 0
 
         def rec():
@@ -170,7 +174,11 @@ def main():
                 attn_lse_merge(o_acc, l_acc, o_cur, l_cur)
                 rec()
         rec()
+        if patch_ev is not None:
+            patch_ev[0].record()
         attn_patch_fwd(q_p, k_p, v_p, k_buf, v_buf, p0, scale=wp["scale"], out=o_p, lse=l_p)
+        if patch_ev is not None:
+            patch_ev[1].record()
         rec()
         rec()
         cfg_combine(eps_u, eps_c, s_cfg, out=eps_out)
@@ -181,20 +189,27 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region ------------------------------------------------------------
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    pevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     sampler = ClockSampler()
     sampler.start()
     t_start.record()
     for k in range(args.steps):
-        step(evs[k])
+        step(patch_ev=pevs[k])
     t_end.record()
     torch.cuda.synchronize()
     clock = sampler.stop()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    patch_ms = [a.elapsed_time(b) for a, b in pevs]
 
-    ring_ms, merge_ms, patch_ms, cfg_ms = [], [], [], []
+    # ---- phase breakdown: instrumented steps after the timed region --------------
+    n_phase = 10
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(n_phase)]
+    for k in range(n_phase):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ring_ms, merge_ms, cfg_ms = [], [], []
     for ev in evs:
         i = 0
         for j in range(nblk):
@@ -203,7 +218,6 @@ def main():
             if j:
                 merge_ms.append(ev[i].elapsed_time(ev[i + 1]))
                 i += 2
-        patch_ms.append(ev[i].elapsed_time(ev[i + 1]))
         i += 2
         cfg_ms.append(ev[i].elapsed_time(ev[i + 1]))
 
@@ -214,6 +228,7 @@ def main():
     f_block = attn_flops(Br, Hr, Nqr, Nkr, dr)
     patch_tflops = f_patch / (patch_us * 1e-6) / 1e12
     phases = {
+        "note": f"ring, merge and CFG per call from {n_phase} instrumented steps after the timed region",
         "ring_block_attn": {"us_per_call": ring_us, "calls_per_step": nblk,
                             "tflops": f_block / (ring_us * 1e-6) / 1e12,
                             "frac_bf16_peak": f_block / (ring_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS},
@@ -222,7 +237,8 @@ def main():
                                   "frac_hbm_peak": merge_bytes / (merge_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                                   "note": "cache-warm: O_b was just written by the block call"},
         "patch_splice_plus_attn": {"us_per_call": patch_us, "tflops": patch_tflops,
-                                   "frac_bf16_peak": patch_tflops / PEAK_BF16_TFLOPS},
+                                   "frac_bf16_peak": patch_tflops / PEAK_BF16_TFLOPS,
+                                   "note": "events around this call in every timed step"},
         "cfg_combine": {"us_per_call": cfg_us, "gbs": cfg_bytes / (cfg_us * 1e-6) / 1e9,
                         "note": "96 KiB working set: launch-latency bound"},
     }
