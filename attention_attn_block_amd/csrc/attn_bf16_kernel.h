@@ -437,16 +437,18 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
           for (int j = 0; j < 8; ++j)
             pb[g][ch][j] = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
         // The normaliser sums the same bf16 weights the product uses; this
-        // lane's share of it also bounds every weight the lane holds.
-        float ls0 = 0.f, ls1 = 0.f;
+        // lane's share of it also bounds every weight the lane holds.  Four
+        // independent accumulation chains keep the dot unit's latency off the
+        // vector phase.
+        float ls0 = 0.f, ls1 = 0.f, ls2 = 0.f, ls3 = 0.f;
 #pragma unroll
         for (int ch = 0; ch < kCH; ++ch) {
           ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][0], pb[g][ch][1]}, ones, ls0, false);
           ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][2], pb[g][ch][3]}, ones, ls1, false);
-          ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][4], pb[g][ch][5]}, ones, ls0, false);
-          ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][6], pb[g][ch][7]}, ones, ls1, false);
+          ls2 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][4], pb[g][ch][5]}, ones, ls2, false);
+          ls3 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][6], pb[g][ch][7]}, ones, ls3, false);
         }
-        ls[g] = ls0 + ls1;
+        ls[g] = (ls0 + ls1) + (ls2 + ls3);
       }
       // Rare: a lane's share of a row's sum exceeds the limit (so some weight
       // there exceeds 2^9), i.e. the row's scores grew well past its reference
