@@ -32,11 +32,19 @@ int attn_split_grid(long long n_items, int Nkv, int n_cu, int min_key_tiles) {
 }
 
 namespace {
-// Compute units of the current device, queried once per device.
-int device_cus() {
+// Compute units of the device a stream runs on, queried once per device.
+int device_cus(hipStream_t stream) {
   static std::atomic<int> cache[64];
+  // The device the work runs on is the stream's, which need not be the
+  // current one; the null stream runs on the current device.
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (stream) {
+    hipDevice_t sd;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return 0;
+    dev = sd;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return 0;
+  }
   if (dev < 0 || dev >= 64) return 0;
   int n = cache[dev].load(std::memory_order_relaxed);
   if (n == 0) {
@@ -52,7 +60,7 @@ hipError_t launch_attn_bf16(const void* Q, const void* K, const void* V, void* O
                             void* ws, bool force_split, hipStream_t stream) {
   const long long n_items = (long long)BH * ((Nq + kAttnRowsPerTile - 1) / kAttnRowsPerTile);
   const int split_grid =
-      ws ? attn_split_grid(n_items, Nkv, device_cus(), force_split ? 0 : kAttnSplitMinKeyTiles) : 0;
+      ws ? attn_split_grid(n_items, Nkv, device_cus(stream), force_split ? 0 : kAttnSplitMinKeyTiles) : 0;
   switch (d) {
 #define DIT_CASE(DD) \
   case DD:           \
