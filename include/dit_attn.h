@@ -26,8 +26,8 @@
  * --------------------------------
  *  - Every pointer is a device pointer owned by the caller and must be 16-byte
  *    aligned.  The library allocates no memory and keeps no per-call state;
- *    the one call that needs scratch (cfg_combine_relmae) takes it from the
- *    caller.
+ *    the calls that need scratch (cfg_combine_relmae, attn_block_fwd_ws,
+ *    attn_patch_fwd_ws) take it from the caller.
  *  - Work is enqueued on `stream` (0 = the null stream) and returns without
  *    synchronising.  Calls on different streams may run concurrently.
  *  - Tensors are row-major and contiguous: [B, H, N, d] with d innermost;
@@ -138,6 +138,9 @@ enum {
  *              different streams race).
  * Returns DIT_ERR_INVALID_ARG for a null, short, misaligned or overlapping
  * workspace or unknown flags, otherwise as attn_block_fwd.
+ * attn_block_workspace_bytes returns the workspace size for a shape (arrival
+ * counters padded to 256 bytes, then four float32 partials of 256 x (d + 1)
+ * per 256-row query tile), or 0 for a non-positive size or an unsupported d.
  */
 long long attn_block_workspace_bytes(int B, int H, int Nq, int Nkv, int d);
 dit_status_t attn_block_fwd_ws(const void* Q, const void* K, const void* V,
