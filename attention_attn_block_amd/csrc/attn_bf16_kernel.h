@@ -178,11 +178,13 @@ __device__ __forceinline__ float row_max(const f32x16* s) {
   return mx;
 }
 
-// NG = query groups of 32 rows per wave.  NG = 2 would let every K and V
-// operand read from LDS (and every tile loaded into LDS) feed twice the
-// matrix work, but it needs one wave per SIMD and about 512 registers, and the
-// compiler then spills heavily; kGroups is 1 (the ping-pong schedule also
-// assumes one group).
+// NG = query groups of 32 rows per wave.  NG = 2 lets every K and V operand
+// read from LDS feed twice the matrix work, but needs one wave per SIMD and
+// about 500 registers.  Built with hand-placed registers (O and Q in AGPRs,
+// the softmax interleaved with the wave's own PV products) it gave the same
+// bits and ran 20% slower: one wave does not hide its vector work behind its
+// own MFMAs, two waves in ping-pong hide about half of it.  kGroups is 1, and
+// the ping-pong schedule assumes one group.
 //
 // SPLIT: the grid is a fixed number of workgroups that share the
 // (query tile, key tile) work evenly, so a query tile's key range may be cut
