@@ -103,9 +103,10 @@ def default_scale(d):
 
 
 def attn_block_workspace(q, k):
-    """Zero-filled workspace for the split calls (attn_block_fwd and
-    attn_block_fwd_merge with workspace=) of q against k's shape.  Reusable by
-    later calls of the same or smaller shape, one call at a time."""
+    """Zero-filled workspace for the split calls (attn_block_fwd,
+    attn_block_fwd_merge and attn_patch_fwd with workspace=) of q against k's
+    shape.  Reusable by later calls of the same or smaller shape, one call at a
+    time."""
     B, H, Nq, d = q.shape
     n = load().attn_block_workspace_bytes(B, H, Nq, k.shape[2], d)
     if n <= 0:
@@ -222,7 +223,8 @@ def attn_patch_fwd(q_p, k_p, v_p, k_buf, v_buf, p0, scale=None, out_dtype=None, 
     if lse is None:
         lse = torch.empty((B, H, Np), dtype=torch.float32, device=dev)
     _dev(q_p, out, lse)
-    if out.shape != (B, H, Np, d) or out.dtype != out_dtype or lse.shape != (B, H, Np):
+    if out.shape != (B, H, Np, d) or out.dtype != out_dtype or lse.shape != (B, H, Np) \
+            or lse.dtype != torch.float32:
         raise ValueError("out/lse shape or dtype mismatch")
     if workspace is not None:
         _dev(q_p, workspace)
@@ -278,7 +280,8 @@ def cfg_combine_relmae(eps_u, eps_c, s, out=None, workspace=None, relmae=None):
         relmae = torch.empty(4, dtype=torch.float32, device=dev)[:1]
     _dev(eps_u, out, workspace, relmae)
     if out.shape != eps_u.shape or out.dtype != torch.float32 or workspace.numel() < nw \
-            or workspace.dtype != torch.float32 or relmae.dtype != torch.float32:
+            or workspace.dtype != torch.float32 or relmae.dtype != torch.float32 \
+            or relmae.numel() < 1:
         raise ValueError("out/workspace/relmae shape or dtype mismatch")
     with torch.cuda.device(dev):
         rc = load().cfg_combine_relmae(eps_u.data_ptr(), eps_c.data_ptr(), out.data_ptr(), n,
