@@ -17,7 +17,7 @@ Prints ONE JSON line.  `value` is attention TFLOP/s over the whole step
 merges, splice and CFG included).  Per-phase times, the roofline of the
 dominant kernel and the fp64 CPU oracle on a bounded sample ride along.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 200] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--no-cpu-baseline]
 
 The default warm-up (about 0.7 s of steps) lets the shader clock settle at its
 steady value under this load before timing; the clock and board power sampled
@@ -46,7 +46,7 @@ ATTN_SRC = os.path.join(ROOT, "attention_attn_block_amd", "csrc", "attn_bf16_ker
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-supplementary", action="store_true")
