@@ -224,6 +224,52 @@ def test_large_scores_stay_finite():
     check_attn(q, k, v, 0.125, torch.float32, "peaked scores")
 
 
+def growing_scores_inputs(B, H, Nq, Nkv, d, seed):
+    """Every 64-key tile's scores exceed the previous tile's by about 32
+    (natural units): key row j is 4 * (j // 64) plus noise, the queries are
+    near 1, the scale is 1/8 at d = 64.  Each new tile's weights would pass any
+    bound against the running reference, so the rescale runs on every tile."""
+    g = torch.Generator().manual_seed(seed)
+    tile = (torch.arange(Nkv) // 64).float()
+    k = (4.0 * tile)[None, None, :, None] + 0.3 * torch.randn(B, H, Nkv, d, generator=g)
+    q = 1.0 + 0.05 * torch.randn(B, H, Nq, d, generator=g)
+    v = torch.randn(B, H, Nkv, d, generator=g)
+    return (q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16))
+
+
+def test_rescale_on_every_tile():
+    """The rare rescale path, taken on every key tile: plain launch, split
+    launch (pieces start with their own reference) and the fused ring step
+    over two blocks."""
+    from attention_attn_block_amd import attn_block_workspace
+    B, H, Nq, Nkv, d = 2, 50, 200, 640, 64
+    q, k, v = growing_scores_inputs(B, H, Nq, Nkv, d, seed=77)
+    scale = 0.125
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale)
+    gq, gk, gv = dev(q), dev(k), dev(v)
+    say("case rescale every tile: plain")
+    O, L = attn_block_fwd(gq, gk, gv, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_f64(O), Or, "rescale plain O")
+    assert_bf16_close(to_f64(L), Lr, "rescale plain LSE")
+    say("case rescale every tile: forced split")
+    ws = attn_block_workspace(gq, gk)
+    O, L = attn_block_fwd(gq, gk, gv, scale=scale, out_dtype=torch.float32, workspace=ws,
+                          force_split=True)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_f64(O), Or, "rescale split O")
+    assert_bf16_close(to_f64(L), Lr, "rescale split LSE")
+    say("case rescale every tile: fused ring step over two blocks")
+    o_acc = torch.zeros(B, H, Nq, d, dtype=torch.float32, device="cuda:0")
+    l_acc = torch.full((B, H, Nq), float("-inf"), dtype=torch.float32, device="cuda:0")
+    for lo, hi in ((0, 320), (320, Nkv)):
+        attn_block_fwd_merge(gq, gk[:, :, lo:hi].contiguous(), gv[:, :, lo:hi].contiguous(), o_acc,
+                             l_acc, scale=scale)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_f64(o_acc), Or, "rescale fused O")
+    assert_bf16_close(to_f64(l_acc), Lr, "rescale fused LSE")
+
+
 @pytest.mark.parametrize("Nkv", [30, 100, 1000])
 def test_ragged_tile_ignores_stale_lds(Nkv):
     """Key rows past a ragged last tile must not carry over whatever an earlier
