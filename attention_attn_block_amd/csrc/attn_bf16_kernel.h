@@ -17,9 +17,12 @@
 //    SIMD (two waves per SIMD, one workgroup per CU).
 //  * Both contractions run on v_mfma_f32_32x32x16_bf16 in the transposed
 //    form S^T = K Q^T and O^T = V^T P^T.  In the 32x32 accumulator layout a
-//    lane then holds 16 values of ONE query row (column = lane % 32), so the
-//    softmax row max / row sum are in-register reductions plus a single
-//    exchange with lane ^ 32, and P never leaves registers: the S^T
+//    lane then holds 16 values of ONE query row (column = lane % 32), shared
+//    with lane ^ 32 only: the row max (taken at the first tile and on a
+//    rescale) and each lane's share of the row sum are in-register
+//    reductions, combined with lane ^ 32 by one exchange, and the two
+//    shares of the sum are added once, in the epilogue.  P never leaves
+//    registers: the S^T
 //    accumulator registers are exactly the B operand of the PV product once
 //    the keys inside each 16-key chunk are visited in the order the
 //    accumulator holds them.
