@@ -401,7 +401,8 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     // every wave executes (the slot count is the same for the whole workgroup).
     // K(t) and V(t) live in LDS buffer t % 2.  Slot 2k starts the loads of
     // K(k+2) and V(k+1) into the buffers whose last readers ran in slot 2k-1;
-    // slot 2k+1 ends by waiting for them.
+    // they land during slot 2k+1, which ends by waiting for them (the barrier
+    // of slot 2k does not).
     const int grp = wave >> 2;
     if (grp == 1) {
       dma_tile(IsK{}, Kh, k_lds[0], kvb);
@@ -583,7 +584,17 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
         }
         dma_wait();
       }
-      __syncthreads();
+      if constexpr ((p & 1) == 0) {
+        // Even slot: its tile loads are read two slots later, after the odd
+        // slot's wait, so they may stay in flight across this barrier.  A
+        // workgroup release fence (__syncthreads) would wait for them here;
+        // only this wave's LDS reads have to be complete.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      } else {
+        __syncthreads();
+      }
     };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
