@@ -35,8 +35,9 @@
 //    tile t's PV product, K one tile ahead of V) with a vector phase (tile
 //    t+1's weights), and the two waves of a SIMD run these phases half a tile
 //    apart, separated by workgroup barriers, so one wave's softmax runs while
-//    the other keeps the matrix core busy.  The wave group in its vector
-//    phase also issues the tile loads.  Inside the matrix phase the LDS
+//    the other keeps the matrix core busy.  Each wave group issues tile
+//    loads in its vector phase (K by one group, V by the other).  Inside the
+//    matrix phase the LDS
 //    operand reads run several products ahead of their use (kKDepth,
 //    kVDepth).
 //  * Workgroup ids are remapped so that all query tiles of a head run on the
@@ -75,7 +76,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 512;   // 8 waves: two per SIMD, ping-pong
-constexpr int kDmaThreads = 256;  // the tile loads are issued by one group of 4 waves
+constexpr int kDmaThreads = 256;  // each tile is loaded by one group of 4 waves
 constexpr int kBc = 64;         // keys per KV tile (a multiple of 32)
 constexpr int kMaxPieces = kAttnMaxPieces;  // SPLIT: workgroups per query tile, at most
 constexpr int kKT = kBc / 32;   // 32-key score accumulators per tile
@@ -399,10 +400,11 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     // Group A runs M(k) in slot 2k and W(k+1) in slot 2k+1; group B runs M(k) in
     // slot 2k+1 and W(k+1) in slot 2k+2.  Every slot ends with a barrier that
     // every wave executes (the slot count is the same for the whole workgroup).
-    // K(t) and V(t) live in LDS buffer t % 2.  Slot 2k starts the loads of
-    // K(k+2) and V(k+1) into the buffers whose last readers ran in slot 2k-1;
-    // they land during slot 2k+1, which ends by waiting for them (the barrier
-    // of slot 2k does not).
+    // K(t) and V(t) live in LDS buffer t % 2.  Each group issues tile loads
+    // in its own vector phase: group B starts K(k+2) in slot 2k, group A
+    // starts V(k+1) in slot 2k+1, each into the buffer whose last readers ran
+    // in slot 2k-1.  Slot 2k+1 ends by waiting for both (the barrier of slot
+    // 2k does not wait).
     const int grp = wave >> 2;
     if (grp == 1) {
       dma_tile(IsK{}, Kh, k_lds[0], kvb);
@@ -569,7 +571,6 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       if constexpr ((p & 1) == 0) {
         if (grp == 1) {  // group B is in its vector phase in even slots
           if (k + 2 < n_tiles) dma_tile(IsK{}, Kh, k_lds[kpar], kvb + (k + 2) * kBc);
-          if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], kvb + (k + 1) * kBc);
         }
         if (grp == 0) {
           if (k < n_tiles) m_phase(KQ{}, KP{}, k);
@@ -577,7 +578,8 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
           if (k >= 1 && k < n_tiles) w_phase(k);
         }
       } else {
-        if (grp == 0) {
+        if (grp == 0) {  // group A is in its vector phase in odd slots
+          if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], kvb + (k + 1) * kBc);
           if (k + 1 < n_tiles) w_phase(k + 1);
         } else {
           if (k < n_tiles) m_phase(KQ{}, KP{}, k);
