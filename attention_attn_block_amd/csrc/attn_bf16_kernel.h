@@ -161,6 +161,23 @@ __device__ __forceinline__ int swz_v(int row) {
   else return 0;
 }
 
+// d = 72: a row is 9 units (36 of the 64 four-byte LDS banks), which no XOR
+// swizzle permutes.  A transposing V read pass covers 4 rows x 4 units, so
+// the V tile places the units of row r at the slots given by a table indexed
+// by r mod 4 (found by exhaustive search) that sends each pass to 16 distinct
+// 4-bank groups.  v9_slot(r, u) is the slot of unit u, v9_unit its inverse
+// (4-bit entries; unit 8 is the last).
+__device__ __forceinline__ int v9_slot(int r, int u) {
+  const unsigned long long t = r == 0 ? 0x387654210ull : r == 1 ? 0x876543210ull
+                             : r == 2 ? 0x87216543ull : 0x576108432ull;
+  return (int)((t >> (4 * u)) & 15);
+}
+__device__ __forceinline__ int v9_unit(int r, int s) {
+  const unsigned long long t = r == 0 ? 0x765438210ull : r == 1 ? 0x876543210ull
+                             : r == 2 ? 0x763210548ull : 0x376821054ull;
+  return (int)((t >> (4 * s)) & 15);
+}
+
 // Lazy rescaling.  The reference max m_ref used for the exponentials is not
 // tracked per tile.  A lane's 32 weights of a tile are accepted while their
 // sum (needed for the normaliser anyway) is at most kLaneSumLimit, which
@@ -253,7 +270,8 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     const int pu = dtid + kDmaThreads * j;
     const int row = pu / G::kOct, col = pu - row * G::kOct;
     koff[j] = (unsigned)(row * D + 8 * (col ^ swz_k<G::kOct>(row))) * 2u;
-    voff[j] = (unsigned)(row * D + 8 * (col ^ swz_v<G::kOct>(row))) * 2u;
+    const int vcol = G::kOct == 9 ? v9_unit(row & 3, col) : (col ^ swz_v<G::kOct>(row));
+    voff[j] = (unsigned)(row * D + 8 * vcol) * 2u;
   }
   // One tile, as buffer loads against a resource that covers exactly the
   // tile's rows inside the block: in the ragged last tile the rows past the
@@ -378,7 +396,10 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 #pragma unroll
     for (int dt = 0; dt < G::kDTiles; ++dt) {
       const int unit = 4 * dt + 2 * (vq & 1) + ((vi & 3) >> 1);
-      v_off[dt] = (v_row * G::kOct + (unit ^ sv)) * 8 + 4 * (vi & 1);
+      // d = 72: the reads past the last unit (output rows never stored) take
+      // unit 8 of the same row, a broadcast.
+      const int slot = G::kOct == 9 ? v9_slot(v_row & 3, unit < 9 ? unit : 8) : (unit ^ sv);
+      v_off[dt] = (v_row * G::kOct + slot) * 8 + 4 * (vi & 1);
     }
 
     f32x16 acc[NG][G::kDTiles];
