@@ -8,4 +8,5 @@ from .ref import (  # noqa: F401
     ref_cfg_relmae,
     ref_lse_merge,
     ref_patch,
+    ref_patch_strided,
 )

@@ -31,6 +31,10 @@ of the operation the pages name, written out in fp64:
                  the device's patch overwrite its rows of the persistent
                  (otherwise stale) KV buffer, then the patch queries attend to
                  the whole buffer.
+* ``ref_patch_strided``  the same step for a patch made of several equal runs
+                 of rows spaced evenly through the buffer (a row slab of a
+                 video that crosses every frame: in frame-major token order
+                 it is one run per frame).
 * ``ref_cfg``    classifier-free guidance, out = eps_u + s (eps_c - eps_u).
 
 Inputs are numpy arrays.  A ``uint16`` array holds bfloat16 bit patterns and
@@ -48,6 +52,7 @@ __all__ = [
     "ref_lse_merge",
     "ref_block_fold",
     "ref_patch",
+    "ref_patch_strided",
     "ref_cfg",
     "ref_cfg_relmae",
 ]
@@ -171,6 +176,43 @@ def ref_patch(Q_p, K_p, V_p, K_buf, V_buf, p0, scale, rows=None):
     V_new = np.array(V_buf, copy=True)
     K_new[:, :, p0:p0 + Np] = K_p
     V_new[:, :, p0:p0 + Np] = V_p
+    O, L = ref_attn(Q_p, K_new, V_new, scale, rows=rows)
+    return O, L, K_new, V_new
+
+
+def ref_patch_strided(Q_p, K_p, V_p, K_buf, V_buf, p0, run_len, run_stride, scale, rows=None):
+    """PipeFusion per-device step for a patch of several runs of buffer rows.
+
+    The pages let devices hold patches of unequal size ("Spatio-Temporal
+    Parallelism for Diffusion Model Inference on Heterogeneous Multi-GPU
+    Systems", abstract) and split the image into patches (xDiT abstract) but
+    do not fix their shape.  A patch that is a band of spatial rows across
+    all frames of a video is, in frame-major token order, not one range of
+    the sequence but one run per frame.  Here the patch is n_runs runs of
+    run_len rows; run r covers buffer rows
+        [p0 + r * run_stride, p0 + r * run_stride + run_len),
+    and the device's patch tensors hold the runs back to back, so patch row
+    r * run_len + i belongs to buffer row p0 + r * run_stride + i.
+    Q_p, K_p, V_p: [B, H, n_runs * run_len, d]; K_buf, V_buf: [B, H, N, d].
+    Each run of K_p / V_p is copied over its rows of the buffer, then the
+    patch queries attend to all N rows (as ``ref_patch``).
+    Returns (O, LSE, K_new, V_new); the input buffers are left untouched.
+    """
+    Np = Q_p.shape[2]
+    N = K_buf.shape[2]
+    if run_len < 1 or Np % run_len:
+        raise ValueError("the patch is not a whole number of runs")
+    n_runs = Np // run_len
+    if n_runs > 1 and run_stride < run_len:
+        raise ValueError("runs overlap")
+    if p0 < 0 or p0 + (n_runs - 1) * run_stride + run_len > N:
+        raise ValueError("patch outside the buffer")
+    K_new = np.array(K_buf, copy=True)
+    V_new = np.array(V_buf, copy=True)
+    for r in range(n_runs):
+        start = p0 + r * run_stride
+        K_new[:, :, start:start + run_len] = K_p[:, :, r * run_len:(r + 1) * run_len]
+        V_new[:, :, start:start + run_len] = V_p[:, :, r * run_len:(r + 1) * run_len]
     O, L = ref_attn(Q_p, K_new, V_new, scale, rows=rows)
     return O, L, K_new, V_new
 

@@ -37,6 +37,10 @@ def compute_cases():
     Op, Lp, Kn, _ = oracle.ref_patch(Q[:, :, :3], K[:, :, :3], V[:, :, :3], K * 0.5, V * 0.5, 4,
                                      1.0 / math.sqrt(8))
     out["patch_np3_p04"] = {"O": Op.tolist(), "LSE": Lp.tolist(), "K_new": Kn.tolist()}
+    Ks = _pattern((1, 2, 9, 8), 1, 1, 2)
+    Op, Lp, Kn, _ = oracle.ref_patch_strided(Q[:, :, :4], K[:, :, :4], V[:, :, :4], Ks, Ks * 0.25,
+                                             1, 2, 5, 1.0 / math.sqrt(8))
+    out["patch_strided_2x2_p01_s5"] = {"O": Op.tolist(), "LSE": Lp.tolist(), "K_new": Kn.tolist()}
     u = _pattern((1, 2, 3, 4), 1, 2, 3)
     c = _pattern((1, 2, 3, 4), 3, 1, 1)
     out["cfg_s4"] = {"out": oracle.ref_cfg(u, c, 4.0).tolist(),

@@ -299,6 +299,78 @@ def pin_patch_splice_and_attend(o):
     assert np.max(np.abs(O - Of[:, :, p0:p0 + Np])) > 1e-4, "stale rows had no effect"
 
 
+def _slab_rows(p0, run_len, run_stride, n_runs):
+    """Buffer row of every patch row, listed one by one (patch row j is row
+    j % run_len of run j // run_len)."""
+    out = []
+    for j in range(n_runs * run_len):
+        out.append(p0 + (j // run_len) * run_stride + j % run_len)
+    return np.array(out, dtype=np.int64)
+
+
+def pin_patch_strided_fresh_is_self_attention(o):
+    """With no staleness a strided patch step gives the patch rows of plain
+    self-attention over the whole sequence, whatever the run layout; and a
+    single run is the contiguous patch step."""
+    r = _rng(16)
+    B, H, N, d = 1, 2, 40, 4
+    X = r.standard_normal((B, H, N, d))
+    K = r.standard_normal((B, H, N, d))
+    V = r.standard_normal((B, H, N, d))
+    Of, Lf = o.ref_attn(X, K, V, 0.5)
+    for p0, run_len, stride, n_runs in ((3, 2, 5, 7), (0, 4, 10, 4), (7, 3, 3, 5), (0, 40, 40, 1)):
+        idx = _slab_rows(p0, run_len, stride, n_runs)
+        O, L, Kn, Vn = o.ref_patch_strided(X[:, :, idx], K[:, :, idx], V[:, :, idx], K, V, p0,
+                                           run_len, stride, 0.5)
+        _close(O, Of[:, :, idx], 1e-13, f"strided fresh O {p0, run_len, stride}")
+        _close(L, Lf[:, :, idx], 1e-13, f"strided fresh lse {p0, run_len, stride}")
+    Ks = K + 0.05 * r.standard_normal(K.shape)
+    Vs = V + 0.05 * r.standard_normal(V.shape)
+    p0, Np = 11, 9
+    a = o.ref_patch_strided(X[:, :, p0:p0 + Np], K[:, :, p0:p0 + Np], V[:, :, p0:p0 + Np], Ks, Vs,
+                            p0, Np, 1000, 0.5)
+    b = o.ref_patch(X[:, :, p0:p0 + Np], K[:, :, p0:p0 + Np], V[:, :, p0:p0 + Np], Ks, Vs, p0, 0.5)
+    for x, y, what in zip(a, b, ("O", "lse", "K", "V")):
+        _close(x, y, 0.0, f"one run = contiguous patch {what}")
+
+
+def pin_patch_strided_splice_rows(o):
+    """The returned buffer is the input with exactly the patch rows replaced,
+    patch row j landing on buffer row p0 + (j // run_len) * stride + j % run_len
+    (rows listed one by one); and the result equals the contiguous patch step
+    on a buffer whose rows are reordered so the runs come first: attention does
+    not depend on the order of the key rows."""
+    r = _rng(17)
+    B, H, N, d = 2, 1, 36, 3
+    p0, run_len, stride, n_runs = 2, 3, 8, 4
+    idx = _slab_rows(p0, run_len, stride, n_runs)
+    Np = idx.size
+    Qp = r.standard_normal((B, H, Np, d))
+    Kp = r.standard_normal((B, H, Np, d))
+    Vp = r.standard_normal((B, H, Np, d))
+    Ks = r.standard_normal((B, H, N, d))
+    Vs = r.standard_normal((B, H, N, d))
+    Ks0, Vs0 = Ks.copy(), Vs.copy()
+    O, L, Kn, Vn = o.ref_patch_strided(Qp, Kp, Vp, Ks, Vs, p0, run_len, stride, 0.7)
+    assert np.array_equal(Ks, Ks0) and np.array_equal(Vs, Vs0), "input buffer modified"
+    want_k, want_v = Ks0.copy(), Vs0.copy()
+    for j in range(Np):
+        want_k[:, :, idx[j]] = Kp[:, :, j]
+        want_v[:, :, idx[j]] = Vp[:, :, j]
+    assert np.array_equal(Kn, want_k) and np.array_equal(Vn, want_v), "strided splice rows wrong"
+    rest = np.array([i for i in range(N) if i not in set(idx.tolist())], dtype=np.int64)
+    perm = np.concatenate([idx, rest])
+    Oc, Lc, _, _ = o.ref_patch(Qp, Kp, Vp, Ks[:, :, perm], Vs[:, :, perm], 0, 0.7)
+    _close(O, Oc, 1e-13, "strided = contiguous on reordered buffer O")
+    _close(L, Lc, 1e-13, "strided = contiguous on reordered buffer lse")
+    for bad in ((p0, run_len, run_len - 1), (N - 5, run_len, stride), (-1, run_len, stride)):
+        try:
+            o.ref_patch_strided(Qp, Kp, Vp, Ks, Vs, bad[0], bad[1], bad[2], 0.7)
+        except ValueError:
+            continue
+        raise AssertionError(f"layout {bad} accepted")
+
+
 # --------------------------------------------------------------------------
 # classifier-free guidance
 # --------------------------------------------------------------------------

@@ -137,6 +137,26 @@ def _m_splice_off_by_one(np_, mod):
     return ("ref_patch", patch)
 
 
+def _m_strided_runs_packed(np_, mod):
+    """Runs placed back to back in the buffer (the stride ignored)."""
+    def patch(Q_p, K_p, V_p, K_buf, V_buf, p0, run_len, run_stride, scale, rows=None):
+        return mod.ref_patch(Q_p, K_p, V_p, K_buf, V_buf, p0, scale, rows=rows)
+    return ("ref_patch_strided", patch)
+
+
+def _m_strided_run_offset(np_, mod):
+    """Run r starts one row late for r >= 1."""
+    def patch(Q_p, K_p, V_p, K_buf, V_buf, p0, run_len, run_stride, scale, rows=None):
+        K_new, V_new = np_.array(K_buf, copy=True), np_.array(V_buf, copy=True)
+        for r in range(Q_p.shape[2] // run_len):
+            st = p0 + r * run_stride + (1 if r else 0)
+            K_new[:, :, st:st + run_len] = K_p[:, :, r * run_len:(r + 1) * run_len]
+            V_new[:, :, st:st + run_len] = V_p[:, :, r * run_len:(r + 1) * run_len]
+        O, L = mod.ref_attn(Q_p, K_new, V_new, scale, rows=rows)
+        return O, L, K_new, V_new
+    return ("ref_patch_strided", patch)
+
+
 def _m_decode_shift(np_, mod):
     def decode(x):
         x = np_.asarray(x)
@@ -155,7 +175,8 @@ def _m_relmae_denominator(np_, mod):
 
 HEAD_MUTANTS = [_m_no_scale, _m_lse_drops_max, _m_normalise_by_max, _m_softmax_wrong_axis, _m_k_for_v]
 MOD_MUTANTS = [_m_merge_sign, _m_merge_lse_no_max, _m_merge_empty_nan, _m_cfg_wrong_base,
-               _m_splice_off_by_one, _m_decode_shift, _m_relmae_denominator]
+               _m_splice_off_by_one, _m_strided_runs_packed, _m_strided_run_offset,
+               _m_decode_shift, _m_relmae_denominator]
 
 
 @pytest.mark.parametrize("mutant", HEAD_MUTANTS + MOD_MUTANTS, ids=lambda f: f.__name__)
