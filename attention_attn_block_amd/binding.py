@@ -19,8 +19,8 @@ DIT_F32, DIT_BF16 = 0, 1
 
 EXPORTS = ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws",
            "attn_block_workspace_bytes", "attn_lse_merge", "attn_patch_fwd", "attn_patch_fwd_ws",
-           "cfg_combine", "cfg_combine_relmae", "cfg_combine_relmae_workspace",
-           "dit_status_string")
+           "cfg_combine", "cfg_combine_relmae", "cfg_combine_relmae_noalloc",
+           "cfg_combine_relmae_workspace", "dit_status_string")
 
 _lib = None
 
@@ -53,10 +53,12 @@ def load():
                                     vp]
     L.cfg_combine.argtypes = [vp, vp, vp, ll, f, vp]
     L.cfg_combine_relmae.argtypes = [vp, vp, vp, ll, f, vp, vp, vp]
+    L.cfg_combine_relmae_noalloc.argtypes = [vp, vp, vp, ll, f, vp, vp]
     L.cfg_combine_relmae_workspace.argtypes = [ll]
     L.cfg_combine_relmae_workspace.restype = ll
     for name in ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws", "attn_lse_merge",
-                 "attn_patch_fwd", "attn_patch_fwd_ws", "cfg_combine", "cfg_combine_relmae"):
+                 "attn_patch_fwd", "attn_patch_fwd_ws", "cfg_combine", "cfg_combine_relmae",
+                 "cfg_combine_relmae_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     L.dit_status_string.argtypes = [ctypes.c_int]
     L.dit_status_string.restype = ctypes.c_char_p

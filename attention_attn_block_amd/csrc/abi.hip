@@ -12,6 +12,9 @@
 #include "../../include/dit_attn.h"
 #include "launch.h"
 
+static_assert(DIT_RELMAE_NOALLOC_MAX_N == dit::kRelmaeStaticMaxN,
+              "the header's limit must match the library's scratch array");
+
 namespace {
 
 constexpr long long kMaxI32 = 0x7fffffffLL;
@@ -254,6 +257,22 @@ dit_status_t cfg_combine_relmae(const float* eps_u, const float* eps_c, float* o
       return DIT_ERR_INVALID_ARG;
   if (overlaps(workspace, wb, relmae, 4)) return DIT_ERR_INVALID_ARG;
   return from_hip(dit::launch_cfg_relmae(eps_u, eps_c, out, n, s, workspace, relmae, stream));
+}
+
+dit_status_t cfg_combine_relmae_noalloc(const float* eps_u, const float* eps_c, float* out,
+                                        long long n, float s, float* relmae, hipStream_t stream) {
+  if (!eps_u || !eps_c || !out || !relmae) return DIT_ERR_INVALID_ARG;
+  if (n <= 0 || !isfinite(s)) return DIT_ERR_INVALID_ARG;
+  if (!aligned16(eps_u) || !aligned16(eps_c) || !aligned16(out) || !aligned16(relmae))
+    return DIT_ERR_INVALID_ARG;
+  if (n > DIT_RELMAE_NOALLOC_MAX_N) return DIT_ERR_UNSUPPORTED;
+  const size_t nb = (size_t)n * sizeof(float);
+  if (out != eps_u && overlaps(out, nb, eps_u, nb)) return DIT_ERR_INVALID_ARG;
+  if (out != eps_c && overlaps(out, nb, eps_c, nb)) return DIT_ERR_INVALID_ARG;
+  const void* all[3] = {eps_u, eps_c, out};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(relmae, 4, all[i], nb)) return DIT_ERR_INVALID_ARG;
+  return from_hip(dit::launch_cfg_relmae_static(eps_u, eps_c, out, n, s, relmae, stream));
 }
 
 const char* dit_status_string(dit_status_t status) {

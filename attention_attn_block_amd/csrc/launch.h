@@ -76,4 +76,12 @@ long long cfg_relmae_work_floats(long long n);
 hipError_t launch_cfg_relmae(const float* u, const float* c, float* out, long long n, float s,
                              float* work, float* relmae, hipStream_t stream);
 
+// The same with the partial sums in the library's own device array of
+// kRelmaeStaticFloats floats (one per GPU) instead of a caller workspace:
+// n up to kRelmaeStaticMaxN.  Allocates nothing.
+constexpr long long kRelmaeStaticFloats = 1LL << 16;            // 256 KiB
+constexpr long long kRelmaeStaticMaxN = kRelmaeStaticFloats / 2 * 4096;  // 2^27
+hipError_t launch_cfg_relmae_static(const float* u, const float* c, float* out, long long n,
+                                    float s, float* relmae, hipStream_t stream);
+
 }  // namespace dit

@@ -8,6 +8,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "launch.h"
@@ -390,6 +392,66 @@ hipError_t launch_cfg_relmae(const float* u, const float* c, float* out, long lo
   cfg_relmae_kernel<<<dim3((unsigned)blocks), kThreads, 0, stream>>>(u, c, out, n, s, work);
   relmae_finish_kernel<<<dim3(1), kFinishThreads, 0, stream>>>(work, (int)blocks, relmae);
   return hipGetLastError();
+}
+
+}  // namespace dit
+
+// ---------------------------------------------------------------------------
+// cfg_combine_relmae without a caller workspace: the per-workgroup partial
+// sums go to a fixed device array of this library instead.  Every GPU the
+// library runs on holds its own copy of the array (loaded with the code
+// object, kept until the process ends).  Host code must not pass the array's
+// name to a kernel -- on the host it is only a stand-in -- so the device
+// address is looked up once per device with hipGetSymbolAddress (that device
+// current) and cached; kernels receive that address.  Calls that overlap on
+// one GPU share the array and race.  Nothing in it needs to start at zero:
+// the first pass writes every entry the second pass reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[dit::kRelmaeStaticFloats];
+
+namespace dit {
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's `scratch`, or null on failure.
+float* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  float* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* addr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || !addr) return nullptr;
+  p = static_cast<float*>(addr);
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+}  // namespace
+
+hipError_t launch_cfg_relmae_static(const float* u, const float* c, float* out, long long n,
+                                    float s, float* relmae, hipStream_t stream) {
+  if (cfg_relmae_work_floats(n) > kRelmaeStaticFloats) return hipErrorInvalidValue;
+  int dev = 0;
+  if (stream) {
+    hipDevice_t sd;
+    const hipError_t e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    dev = sd;
+  } else {
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+  }
+  float* work = scratch_on(dev);
+  if (!work) return hipErrorInvalidSymbol;
+  return launch_cfg_relmae(u, c, out, n, s, work, relmae, stream);
 }
 
 }  // namespace dit

@@ -27,7 +27,8 @@
  *  - Every pointer is a device pointer owned by the caller and must be 16-byte
  *    aligned.  The library allocates no memory and keeps no per-call state;
  *    the calls that need scratch (cfg_combine_relmae, attn_block_fwd_ws,
- *    attn_patch_fwd_ws) take it from the caller.
+ *    attn_patch_fwd_ws) take it from the caller, except
+ *    cfg_combine_relmae_noalloc, which uses a fixed array of the library.
  *  - Work is enqueued on `stream` (0 = the null stream) and returns without
  *    synchronising.  Calls on different streams may run concurrently.
  *  - Tensors are row-major and contiguous: [B, H, N, d] with d innermost;
@@ -250,6 +251,26 @@ long long cfg_combine_relmae_workspace(long long n);
 dit_status_t cfg_combine_relmae(const float* eps_u, const float* eps_c, float* out,
                                 long long n, float s, float* workspace, float* relmae,
                                 hipStream_t stream);
+
+/*
+ * cfg_combine_relmae for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same result, bit for bit, with the per-workgroup partial
+ * sums kept in a fixed 256 KiB device array inside the library instead of a
+ * caller workspace.  Each GPU the library runs on holds its own copy of that
+ * array until the process ends; the call itself allocates nothing.  Calls
+ * that overlap on one GPU (other streams, other threads) share the array and
+ * race: the caller must order them.
+ *   eps_u, eps_c, out, relmae: as cfg_combine_relmae;
+ *   1 <= n <= DIT_RELMAE_NOALLOC_MAX_N (2^27); larger n returns
+ *   DIT_ERR_UNSUPPORTED.
+ * Returns DIT_ERR_HIP if the array's device address cannot be obtained on the
+ * stream's device or the launch fails.
+ */
+#define DIT_RELMAE_NOALLOC_MAX_N (1LL << 27)
+dit_status_t cfg_combine_relmae_noalloc(const float* eps_u, const float* eps_c, float* out,
+                                        long long n, float s, float* relmae,
+                                        hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char* dit_status_string(dit_status_t status);

@@ -289,6 +289,23 @@ def test_cfg_combine_relmae_rejects(lib, kw, code):
     assert relmae(lib, **kw) == code
 
 
+def relmae_noalloc(lib, **kw):
+    a = dict(u=ptr(0), c=ptr(1), o=ptr(2), n=8192, s=4.0, r=ptr(4))
+    a.update(kw)
+    return lib.cfg_combine_relmae_noalloc(a["u"], a["c"], a["o"], a["n"], a["s"], a["r"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(u=None), INV), (dict(c=None), INV), (dict(o=None), INV), (dict(r=None), INV),
+    (dict(n=0), INV), (dict(n=-3), INV), (dict(s=math.nan), INV), (dict(r=ptr(4, 8)), INV),
+    (dict(o=ptr(1, 16)), INV),                   # out partially overlaps eps_c
+    (dict(r=ptr(2, 64)), INV),                   # result inside out
+    (dict(n=(1 << 27) + 1), UNS),                # beyond the library's fixed array
+])
+def test_cfg_combine_relmae_noalloc_rejects(lib, kw, code):
+    assert relmae_noalloc(lib, **kw) == code
+
+
 # ---------------------------------------------------------------------------
 # Python binding: marshalling checks that never reach the library
 # ---------------------------------------------------------------------------
