@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     attn_block_workspace,
     attn_lse_merge,
     attn_patch_fwd,
+    attn_patch_fwd_strided,
     cfg_combine,
     cfg_combine_relmae,
     default_scale,

@@ -19,6 +19,7 @@ DIT_F32, DIT_BF16 = 0, 1
 
 EXPORTS = ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws",
            "attn_block_workspace_bytes", "attn_lse_merge", "attn_patch_fwd", "attn_patch_fwd_ws",
+           "attn_patch_fwd_strided",
            "cfg_combine", "cfg_combine_relmae", "cfg_combine_relmae_noalloc",
            "cfg_combine_relmae_workspace", "dit_status_string")
 
@@ -51,13 +52,16 @@ def load():
     L.attn_patch_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     L.attn_patch_fwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, ll,
                                     vp]
+    L.attn_patch_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i,
+                                         i, vp, ll, vp]
     L.cfg_combine.argtypes = [vp, vp, vp, ll, f, vp]
     L.cfg_combine_relmae.argtypes = [vp, vp, vp, ll, f, vp, vp, vp]
     L.cfg_combine_relmae_noalloc.argtypes = [vp, vp, vp, ll, f, vp, vp]
     L.cfg_combine_relmae_workspace.argtypes = [ll]
     L.cfg_combine_relmae_workspace.restype = ll
     for name in ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws", "attn_lse_merge",
-                 "attn_patch_fwd", "attn_patch_fwd_ws", "cfg_combine", "cfg_combine_relmae",
+                 "attn_patch_fwd", "attn_patch_fwd_ws", "attn_patch_fwd_strided", "cfg_combine",
+                 "cfg_combine_relmae",
                  "cfg_combine_relmae_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     L.dit_status_string.argtypes = [ctypes.c_int]
@@ -106,9 +110,10 @@ def default_scale(d):
 
 def attn_block_workspace(q, k):
     """Zero-filled workspace for the split calls (attn_block_fwd,
-    attn_block_fwd_merge and attn_patch_fwd with workspace=) of q against k's
-    shape.  Reusable by later calls of the same or smaller shape, one call at a
-    time."""
+    attn_block_fwd_merge, attn_patch_fwd and attn_patch_fwd_strided with
+    workspace=) of q against k's shape.  Reusable by later calls with no more
+    256-row query tiles (B * H * ceil(Nq / 256)), at any head dim, one call at
+    a time."""
     B, H, Nq, d = q.shape
     n = load().attn_block_workspace_bytes(B, H, Nq, k.shape[2], d)
     if n <= 0:
@@ -246,6 +251,51 @@ def attn_patch_fwd(q_p, k_p, v_p, k_buf, v_buf, p0, scale=None, out_dtype=None, 
                                    lse.data_ptr(), B, H, Np, N, int(p0), d, scale,
                                    _dtype(q_p.dtype), _dtype(out_dtype), _stream(dev))
     _check("attn_patch_fwd", rc)
+    return out, lse
+
+
+def attn_patch_fwd_strided(q_p, k_p, v_p, k_buf, v_buf, p0, run_len, run_stride, scale=None,
+                           out_dtype=None, out=None, lse=None, workspace=None):
+    """Patch step for a patch of several runs of buffer rows: the patch rows
+    (q_p, k_p, v_p: [B, H, Np, d], Np a multiple of run_len) are n_runs =
+    Np / run_len runs back to back, run r belonging to buffer rows
+    [p0 + r * run_stride, +run_len).  Splices each run of k_p/v_p into
+    k_buf/v_buf (in place), then attends q_p to the whole buffer.  Returns
+    (O, LSE).  workspace: as attn_patch_fwd."""
+    dev = _dev(q_p, k_p, v_p, k_buf, v_buf)
+    B, H, Np, d = q_p.shape
+    N = k_buf.shape[2]
+    if k_p.shape != q_p.shape or v_p.shape != q_p.shape or k_buf.shape != (B, H, N, d) \
+            or v_buf.shape != k_buf.shape \
+            or len({t.dtype for t in (q_p, k_p, v_p, k_buf, v_buf)}) != 1:
+        raise ValueError("patch/buffer shapes or dtypes disagree")
+    run_len = int(run_len)
+    if run_len < 1 or Np % run_len:
+        raise ValueError("the patch is not a whole number of runs of run_len rows")
+    n_runs = Np // run_len
+    out_dtype = q_p.dtype if out_dtype is None else out_dtype
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, Np, d), dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, Np), dtype=torch.float32, device=dev)
+    _dev(q_p, out, lse)
+    if out.shape != (B, H, Np, d) or out.dtype != out_dtype or lse.shape != (B, H, Np) \
+            or lse.dtype != torch.float32:
+        raise ValueError("out/lse shape or dtype mismatch")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev(q_p, workspace)
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor (attn_block_workspace)")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    with torch.cuda.device(dev):
+        rc = load().attn_patch_fwd_strided(q_p.data_ptr(), k_p.data_ptr(), v_p.data_ptr(),
+                                           k_buf.data_ptr(), v_buf.data_ptr(), out.data_ptr(),
+                                           lse.data_ptr(), B, H, run_len, n_runs, int(run_stride),
+                                           N, int(p0), d, scale, _dtype(q_p.dtype),
+                                           _dtype(out_dtype), ws_ptr, ws_bytes, _stream(dev))
+    _check("attn_patch_fwd_strided", rc)
     return out, lse
 
 

@@ -76,11 +76,13 @@ dit_status_t run_attn(const void* Q, const void* K, const void* V, void* O, floa
                                        BH, Nq, Nkv, d, scale, merge, stream));
 }
 
-// attn_patch_fwd with an optional split workspace (null: plain launch).
+// The patch step for a patch of n_runs runs of run_len buffer rows, run r at
+// rows [p0 + r * run_stride, +run_len) (one run: a contiguous patch), with an
+// optional split workspace (null: plain launch).
 dit_status_t patch_fwd(const void* Q_p, const void* K_p, const void* V_p, void* K_buf, void* V_buf,
-                       void* O, float* LSE, int B, int H, int Np, int N, int p0, int d, float scale,
-                       dit_dtype_t in_dtype, dit_dtype_t out_dtype, void* ws, long long ws_bytes,
-                       hipStream_t stream);
+                       void* O, float* LSE, int B, int H, int run_len, int n_runs, int run_stride,
+                       int N, int p0, int d, float scale, dit_dtype_t in_dtype,
+                       dit_dtype_t out_dtype, void* ws, long long ws_bytes, hipStream_t stream);
 
 }  // namespace
 
@@ -118,7 +120,7 @@ dit_status_t attn_block_fwd_merge(const void* Q, const void* K, const void* V, v
 long long attn_block_workspace_bytes(int B, int H, int Nq, int Nkv, int d) {
   if (B <= 0 || H <= 0 || Nq <= 0 || Nkv <= 0 || !head_dim_ok(d)) return 0;
   const long long items = (long long)B * H * ((Nq + dit::kAttnRowsPerTile - 1) / dit::kAttnRowsPerTile);
-  return dit::attn_split_layout(items, d).bytes;
+  return dit::attn_split_workspace_bytes(items);
 }
 
 dit_status_t attn_block_fwd_ws(const void* Q, const void* K, const void* V, void* O_acc,
@@ -167,8 +169,8 @@ dit_status_t attn_patch_fwd(const void* Q_p, const void* K_p, const void* V_p, v
                             void* V_buf, void* O, float* LSE, int B, int H, int Np, int N, int p0,
                             int d, float scale, dit_dtype_t in_dtype, dit_dtype_t out_dtype,
                             hipStream_t stream) {
-  return patch_fwd(Q_p, K_p, V_p, K_buf, V_buf, O, LSE, B, H, Np, N, p0, d, scale, in_dtype,
-                   out_dtype, nullptr, 0, stream);
+  return patch_fwd(Q_p, K_p, V_p, K_buf, V_buf, O, LSE, B, H, Np, 1, Np, N, p0, d, scale,
+                   in_dtype, out_dtype, nullptr, 0, stream);
 }
 
 dit_status_t attn_patch_fwd_ws(const void* Q_p, const void* K_p, const void* V_p, void* K_buf,
@@ -177,19 +179,36 @@ dit_status_t attn_patch_fwd_ws(const void* Q_p, const void* K_p, const void* V_p
                                dit_dtype_t out_dtype, void* workspace, long long workspace_bytes,
                                hipStream_t stream) {
   if (!workspace) return DIT_ERR_INVALID_ARG;
-  return patch_fwd(Q_p, K_p, V_p, K_buf, V_buf, O, LSE, B, H, Np, N, p0, d, scale, in_dtype,
-                   out_dtype, workspace, workspace_bytes, stream);
+  return patch_fwd(Q_p, K_p, V_p, K_buf, V_buf, O, LSE, B, H, Np, 1, Np, N, p0, d, scale,
+                   in_dtype, out_dtype, workspace, workspace_bytes, stream);
+}
+
+dit_status_t attn_patch_fwd_strided(const void* Q_p, const void* K_p, const void* V_p,
+                                    void* K_buf, void* V_buf, void* O, float* LSE, int B, int H,
+                                    int run_len, int n_runs, int run_stride, int N, int p0, int d,
+                                    float scale, dit_dtype_t in_dtype, dit_dtype_t out_dtype,
+                                    void* workspace, long long workspace_bytes,
+                                    hipStream_t stream) {
+  return patch_fwd(Q_p, K_p, V_p, K_buf, V_buf, O, LSE, B, H, run_len, n_runs, run_stride, N, p0,
+                   d, scale, in_dtype, out_dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
 
 namespace {
 dit_status_t patch_fwd(const void* Q_p, const void* K_p, const void* V_p, void* K_buf, void* V_buf,
-                       void* O, float* LSE, int B, int H, int Np, int N, int p0, int d, float scale,
-                       dit_dtype_t in_dtype, dit_dtype_t out_dtype, void* ws, long long ws_bytes,
-                       hipStream_t stream) {
+                       void* O, float* LSE, int B, int H, int run_len, int n_runs, int run_stride,
+                       int N, int p0, int d, float scale, dit_dtype_t in_dtype,
+                       dit_dtype_t out_dtype, void* ws, long long ws_bytes, hipStream_t stream) {
   if (!K_p || !V_p || !K_buf || !V_buf) return DIT_ERR_INVALID_ARG;
-  if (N <= 0 || Np <= 0 || p0 < 0 || (long long)p0 + Np > N) return DIT_ERR_INVALID_ARG;
+  if (N <= 0 || run_len <= 0 || n_runs <= 0 || p0 < 0) return DIT_ERR_INVALID_ARG;
+  // Runs must not overlap (and go forward); the last must end inside the buffer.
+  if (n_runs > 1 && run_stride < run_len) return DIT_ERR_INVALID_ARG;
+  const long long last_end = (long long)p0 + (long long)(n_runs - 1) * (n_runs > 1 ? run_stride : 0) +
+                             run_len;
+  if (last_end > N) return DIT_ERR_INVALID_ARG;
+  // The runs are disjoint rows of [0, N), so Np <= N fits an int.
+  const int Np = (int)((long long)run_len * n_runs);
   size_t qb, kvb, ob, lb;
   const dit_status_t st = check_attn(Q_p, K_buf, V_buf, O, LSE, B, H, Np, N, d, scale,
                                      (int)in_dtype, (int)out_dtype, &qb, &kvb, &ob, &lb);
@@ -215,8 +234,10 @@ dit_status_t patch_fwd(const void* Q_p, const void* K_p, const void* V_p, void* 
   }
 
   const long long row_units = (long long)d * (long long)elt_size(in_dtype) / 16;
-  hipError_t e = dit::launch_splice2(K_p, K_buf, V_p, V_buf, B * H, (long long)Np * row_units,
-                                     (long long)N * row_units, (long long)p0 * row_units, stream);
+  hipError_t e = dit::launch_splice2(K_p, K_buf, V_p, V_buf, (long long)B * H, n_runs,
+                                     (long long)run_len * row_units, (long long)N * row_units,
+                                     (long long)(n_runs > 1 ? run_stride : 0) * row_units,
+                                     (long long)p0 * row_units, stream);
   if (e != hipSuccess) return DIT_ERR_HIP;
   return run_attn(Q_p, K_buf, V_buf, O, LSE, B * H, Np, N, d, scale, in_dtype, out_dtype, false,
                   ws, false, stream);

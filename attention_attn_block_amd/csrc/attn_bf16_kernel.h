@@ -217,7 +217,7 @@ template <int D, int NG, bool OUT_F32, bool MERGE, bool SPLIT>
 __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     void* __restrict__ Out, float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, float c2,
-    int n_items, unsigned* __restrict__ ws_count, float* __restrict__ ws_part) {
+    int n_items, char* __restrict__ ws) {
   using G = Geo<D>;
   constexpr int kRowsWG = (kThreads / 64) * 32 * NG;  // query rows per workgroup
   // K and V tiles: kBc rows of kOct 16-byte units each, unit-swizzled (see
@@ -694,13 +694,17 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       // log2 units -- and are combined in key order, so the result is the same
       // bits whichever piece combines.
       constexpr int kSlot = kRowsWG * (D + 1);  // floats per partial: O rows, then LSE
+      static_assert(kSlot * 4 <= kAttnSplitSlotBytes, "a partial must fit its workspace slot");
+      constexpr long long kSlotStride = kAttnSplitSlotBytes / 4;  // floats between slots
       const long long total = (long long)n_items * n_all;
       // Workgroup whose range holds unit x (ranges start at total * w / nblk).
       auto owner = [&](long long x) { return ((x + 1) * nblk + total - 1) / total - 1; };
       const long long w_first = owner((long long)item * n_all);
       const int n_pieces = (int)(owner((long long)item * n_all + n_all - 1) - w_first + 1);
       const int j_piece = (int)(logical - w_first);
-      float* slots = ws_part + (size_t)item * kMaxPieces * kSlot;
+      // This tile's workspace record: arrival counter, then the partial slots.
+      char* rec = ws + (size_t)item * kAttnSplitItemBytes;
+      float* slots = reinterpret_cast<float*>(rec + 256);
       float lse_own[NG];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -718,8 +722,8 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       // invalidate -- those would also drop the K/V tiles other workgroups are
       // reusing from L2.
       auto slot_rsrc = [&](int j) {
-        return __builtin_amdgcn_make_buffer_rsrc(slots + (size_t)j * kSlot, (short)0, kSlot * 4,
-                                                 kBufferFlags);
+        return __builtin_amdgcn_make_buffer_rsrc(slots + (size_t)j * kSlotStride, (short)0,
+                                                 kSlot * 4, kBufferFlags);
       };
       constexpr int kCoherent = 16;  // sc1
       auto publish = [&]() {
@@ -758,7 +762,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       // for another.  The counter is a relaxed device-scope atomic; each
       // arrival first waits until this workgroup's coherent stores are
       // acknowledged.
-      unsigned* cnt = ws_count + item;
+      unsigned* cnt = reinterpret_cast<unsigned*>(rec);
       auto arrive = [&](unsigned add) -> unsigned {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // own published stores acknowledged
         __syncthreads();
@@ -903,7 +907,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 // Launch for one head dim (explicitly instantiated in the attn_bf16_d*.hip
 // files so the instantiations compile in parallel).  split_grid > 0 selects
 // the SPLIT kernel on that many workgroups, with `ws` laid out as
-// attn_split_layout describes.
+// attn_split_workspace_bytes describes (one record per query tile).
 template <int D>
 hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH,
                          int Nq, int Nkv, float scale, bool out_f32, bool merge, int split_grid,
@@ -919,7 +923,7 @@ hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, f
   const __bf16* k = static_cast<const __bf16*>(K);
   const __bf16* v = static_cast<const __bf16*>(V);
   using Kern = void (*)(const __bf16*, const __bf16*, const __bf16*, void*, float*, int, int, int,
-                        float, int, unsigned*, float*);
+                        float, int, char*);
   const bool split = split_grid > 0;
   // [out_f32][merge][split]
   static constexpr Kern kKernels[2][2][2] = {
@@ -928,15 +932,9 @@ hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, f
       {{attn_fwd_bf16_kernel<D, NG, true, false, false>, attn_fwd_bf16_kernel<D, NG, true, false, true>},
        {attn_fwd_bf16_kernel<D, NG, true, true, false>, attn_fwd_bf16_kernel<D, NG, true, true, true>}}};
   const Kern kern = kKernels[out_f32][merge][split];
-  unsigned* ws_count = nullptr;
-  float* ws_part = nullptr;
-  if (split) {
-    const AttnSplitLayout lay = attn_split_layout(n_items, D);
-    ws_count = static_cast<unsigned*>(ws);
-    ws_part = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.part_offset);
-  }
   const dim3 grid((unsigned)(split ? split_grid : n_items));
-  kern<<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2, n_items, ws_count, ws_part);
+  kern<<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2, n_items,
+                                      split ? static_cast<char*>(ws) : nullptr);
   return hipGetLastError();
 }
 

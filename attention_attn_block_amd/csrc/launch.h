@@ -13,17 +13,18 @@ constexpr int kAttnRowsPerTile = 256;
 constexpr int kAttnKeysPerTile = 64;
 constexpr int kAttnMaxPieces = 4;
 
-// Workspace of the split launch for `n_items` query tiles of head dim d: one
-// arrival counter per tile (uint32, zero between calls), then kAttnMaxPieces
-// fp32 partials per tile (O rows, then LSE).
-struct AttnSplitLayout {
-  long long part_offset;  // bytes; the counters occupy [0, part_offset)
-  long long bytes;        // total
-};
-inline AttnSplitLayout attn_split_layout(long long n_items, int d) {
-  const long long counters = (n_items * 4 + 255) / 256 * 256;
-  const long long part = (long long)kAttnRowsPerTile * (d + 1) * 4;
-  return {counters, counters + n_items * kAttnMaxPieces * part};
+// Workspace of the split launch: one record of kAttnSplitItemBytes per query
+// tile, the same size and layout for every shape and head dim, so that a
+// workspace made for one call serves any later call with no more query tiles
+// (at any head dim) without a counter ever landing on another call's
+// partials.  Record i, at byte i * kAttnSplitItemBytes:
+//   [0, 4)                          arrival counter (uint32, zero between calls)
+//   [256 + j * kAttnSplitSlotBytes)  partial j < kAttnMaxPieces of the tile:
+//                                    fp32 O rows [256][d], then LSE [256]
+constexpr long long kAttnSplitSlotBytes = (long long)kAttnRowsPerTile * (128 + 1) * 4;
+constexpr long long kAttnSplitItemBytes = 256 + kAttnMaxPieces * kAttnSplitSlotBytes;
+inline long long attn_split_workspace_bytes(long long n_items) {
+  return n_items * kAttnSplitItemBytes;
 }
 
 // Workgroup count for the split launch on a device with n_cu compute units,
@@ -41,8 +42,8 @@ constexpr int kAttnSplitMinKeyTiles = 96;
 // Attention with bfloat16 Q/K/V (matrix cores), fp32 or bf16 output.  With
 // `merge`, (O, LSE) hold a running partial that the block's result is folded
 // into (LSE = -inf: empty) instead of being overwritten.  A non-null `ws`
-// (attn_split_layout bytes, counters zero) allows the split launch for blocks
-// of at least kAttnSplitMinKeyTiles key tiles, or of any length with
+// (attn_split_workspace_bytes, counters zero) allows the split launch for
+// blocks of at least kAttnSplitMinKeyTiles key tiles, or of any length with
 // force_split.
 hipError_t launch_attn_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                             int BH, int Nq, int Nkv, int d, float scale, bool out_f32, bool merge,
@@ -58,11 +59,13 @@ hipError_t launch_attn_f32(const float* Q, const float* K, const float* V, float
 hipError_t launch_lse_merge(void* Oa, float* La, const void* Ob, const float* Lb,
                             long long rows, int d, bool bf16, hipStream_t stream);
 
-// Copy `nseg` segments of `seg_units` 16-byte units from src (packed) into
-// dst, where segment i starts at unit i * dst_seg_stride + dst_offset.
-// Two independent copies (K and V) run in one launch.
+// Copy n_bh * n_runs segments of `run_units` 16-byte units from src (packed,
+// segment s at unit s * run_units) into dst, where segment s = bh * n_runs + r
+// starts at unit bh * dst_bh_stride + r * dst_run_stride + dst_offset.  Two
+// independent copies (K and V) run in one launch.  Any segment count.
 hipError_t launch_splice2(const void* src0, void* dst0, const void* src1, void* dst1,
-                          int nseg, long long seg_units, long long dst_seg_stride,
+                          long long n_bh, int n_runs, long long run_units,
+                          long long dst_bh_stride, long long dst_run_stride,
                           long long dst_offset, hipStream_t stream);
 
 // out = u + s * (c - u) over n floats.

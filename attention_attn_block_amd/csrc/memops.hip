@@ -114,36 +114,44 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(void* Oa_, float* L
 
 // ---------------------------------------------------------------------------
 // PipeFusion splice (xDiT abstract): the fresh K and V of this device's patch
-// overwrite their rows of the persistent KV buffer.  blockIdx.z picks K or V,
-// blockIdx.y the (batch, head) segment.
+// overwrite their rows of the persistent KV buffer.  The patch is one run of
+// rows per (batch, head), or several evenly spaced runs (a band of spatial
+// rows across every frame of a video); each (batch, head, run) is a segment.
+// blockIdx.z picks K or V; blockIdx.y strides over the segments.
 // ---------------------------------------------------------------------------
 template <int U>
 __global__ __launch_bounds__(kThreads) void splice2_kernel(const u32x4* __restrict__ src0,
                                                           u32x4* __restrict__ dst0,
                                                           const u32x4* __restrict__ src1,
                                                           u32x4* __restrict__ dst1,
-                                                          long long seg_units,
-                                                          long long dst_seg_stride,
+                                                          long long nseg, int n_runs,
+                                                          long long run_units,
+                                                          long long dst_bh_stride,
+                                                          long long dst_run_stride,
                                                           long long dst_offset) {
   const u32x4* src = blockIdx.z ? src1 : src0;
   u32x4* dst = blockIdx.z ? dst1 : dst0;
-  const long long seg = blockIdx.y;
-  const u32x4* s = src + seg * seg_units;
-  u32x4* t = dst + seg * dst_seg_stride + dst_offset;
-  // Each pass moves U groups per lane, all loads issued before the stores
-  // (plain accesses: the fresh patch is usually cache-resident).
-  const long long pass = (long long)gridDim.x * kThreads * U;
-  for (long long b0 = (long long)blockIdx.x * kThreads * U + threadIdx.x; b0 < seg_units; b0 += pass) {
-    u32x4 v[U];
+  for (long long seg = blockIdx.y; seg < nseg; seg += gridDim.y) {
+    const long long bh = seg / n_runs;
+    const long long r = seg - bh * n_runs;
+    const u32x4* s = src + seg * run_units;
+    u32x4* t = dst + bh * dst_bh_stride + r * dst_run_stride + dst_offset;
+    // Each pass moves U groups per lane, all loads issued before the stores
+    // (plain accesses: the fresh patch is usually cache-resident).
+    const long long pass = (long long)gridDim.x * kThreads * U;
+    for (long long b0 = (long long)blockIdx.x * kThreads * U + threadIdx.x; b0 < run_units;
+         b0 += pass) {
+      u32x4 v[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const long long i = b0 + (long long)k * kThreads;
-      if (i < seg_units) v[k] = s[i];
-    }
+      for (int k = 0; k < U; ++k) {
+        const long long i = b0 + (long long)k * kThreads;
+        if (i < run_units) v[k] = s[i];
+      }
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const long long i = b0 + (long long)k * kThreads;
-      if (i < seg_units) t[i] = v[k];
+      for (int k = 0; k < U; ++k) {
+        const long long i = b0 + (long long)k * kThreads;
+        if (i < run_units) t[i] = v[k];
+      }
     }
   }
 }
@@ -351,16 +359,20 @@ hipError_t launch_lse_merge(void* Oa, float* La, const void* Ob, const float* Lb
   return hipGetLastError();
 }
 
-hipError_t launch_splice2(const void* src0, void* dst0, const void* src1, void* dst1, int nseg,
-                          long long seg_units, long long dst_seg_stride, long long dst_offset,
-                          hipStream_t stream) {
-  long long bx = (seg_units + kThreads * kSpliceUnroll - 1) / (kThreads * kSpliceUnroll);
-  if (bx < 1) bx = 1;
+hipError_t launch_splice2(const void* src0, void* dst0, const void* src1, void* dst1,
+                          long long n_bh, int n_runs, long long run_units,
+                          long long dst_bh_stride, long long dst_run_stride,
+                          long long dst_offset, hipStream_t stream) {
+  if (n_bh <= 0 || n_runs <= 0 || run_units <= 0) return hipErrorInvalidValue;
+  const long long nseg = n_bh * n_runs;
+  long long bx = (run_units + kThreads * kSpliceUnroll - 1) / (kThreads * kSpliceUnroll);
   if (bx > 65535) bx = 65535;
-  if (nseg > 65535) return hipErrorInvalidValue;
-  splice2_kernel<kSpliceUnroll><<<dim3((unsigned)bx, (unsigned)nseg, 2), kThreads, 0, stream>>>(
+  // Segments past the y range of the grid are taken by the kernel's stride loop.
+  const long long by = nseg < 65535 ? nseg : 65535;
+  splice2_kernel<kSpliceUnroll><<<dim3((unsigned)bx, (unsigned)by, 2), kThreads, 0, stream>>>(
       static_cast<const u32x4*>(src0), static_cast<u32x4*>(dst0), static_cast<const u32x4*>(src1),
-      static_cast<u32x4*>(dst1), seg_units, dst_seg_stride, dst_offset);
+      static_cast<u32x4*>(dst1), nseg, n_runs, run_units, dst_bh_stride, dst_run_stride,
+      dst_offset);
   return hipGetLastError();
 }
 

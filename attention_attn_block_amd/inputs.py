@@ -25,6 +25,10 @@ public dataset or benchmark is named there):
                     queries at token offset 8192; the KV buffer holds the
                     fresh K/V plus N(0, 0.05^2) noise (stale), the fresh patch
                     holds the un-noised K/V of its rows.
+* ``video_slab_patch``  the same video cut into 4 patches of 16 spatial rows
+                    across all 8 frames: in frame-major token order patch p is
+                    8 runs of 1024 tokens, one per frame (runs start at
+                    p * 1024 + f * 4096); same draws and staleness.
 """
 
 import math
@@ -41,6 +45,7 @@ __all__ = [
     "pixart_1024",
     "ring_2048px",
     "video_patch",
+    "video_slab_patch",
     "cfg_inputs",
     "make",
 ]
@@ -158,6 +163,38 @@ def video_patch(seed=None, p0=None, N=None, Np=None, H=None):
                 scale=default_scale(d))
 
 
+def video_slab_patch(seed=None, p=1, frames=8, height=64, width=64, slab=16, H=None):
+    """A row-slab patch of the video workload: spatial rows [p*slab, (p+1)*slab)
+    of every frame.  Tokens are frame-major (frame, row, column), so the patch
+    is `frames` runs of slab*width tokens, run f starting at token
+    p*slab*width + f*height*width.  Draw order and staleness as video_patch
+    (Q_p; K, V for all rows; noise_K, noise_V); the fresh patch holds the
+    un-noised K/V of the patch rows, runs back to back.  Returns the tensors
+    plus p0, run_len, run_stride and n_runs."""
+    w = WORKLOADS["video_patch"]
+    g = _gen(w["seed"] if seed is None else seed)
+    B, d = w["B"], w["d"]
+    H = w["H"] if H is None else H
+    N = frames * height * width
+    run_len, run_stride, n_runs = slab * width, height * width, frames
+    p0 = p * slab * width
+    Np = run_len * n_runs
+    rows = torch.cat([torch.arange(p0 + f * run_stride, p0 + f * run_stride + run_len)
+                      for f in range(n_runs)])
+    q_p = randn((B, H, Np, d), g)
+    k = randn((B, H, N, d), g, "f32")
+    v = randn((B, H, N, d), g, "f32")
+    nk = randn((B, H, N, d), g, "f32", std=w["stale_std"])
+    nv = randn((B, H, N, d), g, "f32", std=w["stale_std"])
+    k_buf = (k + nk).to(torch.bfloat16)
+    v_buf = (v + nv).to(torch.bfloat16)
+    k_p = k[:, :, rows].to(torch.bfloat16).contiguous()
+    v_p = v[:, :, rows].to(torch.bfloat16).contiguous()
+    del k, v, nk, nv
+    return dict(q_p=q_p, k_p=k_p, v_p=v_p, k_buf=k_buf, v_buf=v_buf, p0=p0, run_len=run_len,
+                run_stride=run_stride, n_runs=n_runs, scale=default_scale(d))
+
+
 def make(name, **kw):
     return {
         "tiny_f32": tiny_f32,
@@ -165,4 +202,5 @@ def make(name, **kw):
         "pixart_1024": pixart_1024,
         "ring_2048px": ring_2048px,
         "video_patch": video_patch,
+        "video_slab_patch": video_slab_patch,
     }[name](**kw)

@@ -27,7 +27,8 @@
  *  - Every pointer is a device pointer owned by the caller and must be 16-byte
  *    aligned.  The library allocates no memory and keeps no per-call state;
  *    the calls that need scratch (cfg_combine_relmae, attn_block_fwd_ws,
- *    attn_patch_fwd_ws) take it from the caller, except
+ *    attn_patch_fwd_ws, attn_patch_fwd_strided with a workspace) take it
+ *    from the caller, except
  *    cfg_combine_relmae_noalloc, which uses a fixed array of the library.
  *  - Work is enqueued on `stream` (0 = the null stream) and returns without
  *    synchronising.  Calls on different streams may run concurrently.
@@ -134,14 +135,18 @@ enum {
  *   workspace: device memory of at least attn_block_workspace_bytes(...)
  *              bytes, 256-byte aligned, owned by the caller, overlapping no
  *              tensor.  It must be zero-filled before its first use; every
- *              call leaves its arrival counters at zero again.  One workspace
- *              serves one call at a time (calls that share a workspace on
- *              different streams race).
+ *              call leaves its arrival counters at zero again, so a workspace
+ *              made for one shape serves any later call with no more query
+ *              tiles, at any head dim.  One workspace serves one call at a
+ *              time (calls that share a workspace on different streams race).
  * Returns DIT_ERR_INVALID_ARG for a null, short, misaligned or overlapping
  * workspace or unknown flags, otherwise as attn_block_fwd.
- * attn_block_workspace_bytes returns the workspace size for a shape (arrival
- * counters padded to 256 bytes, then four float32 partials of 256 x (d + 1)
- * per 256-row query tile), or 0 for a non-positive size or an unsupported d.
+ * attn_block_workspace_bytes returns the workspace size for a shape, or 0 for
+ * a non-positive size or an unsupported d: one record of 528640 bytes per
+ * 256-row query tile (B * H * ceil(Nq / 256) records), whatever the head dim
+ * -- an arrival counter in the record's first 256 bytes, then four float32
+ * partials of 256 x (128 + 1).  A counter therefore sits at the same place
+ * for every shape and never under another call's partials.
  */
 long long attn_block_workspace_bytes(int B, int H, int Nq, int Nkv, int d);
 dit_status_t attn_block_fwd_ws(const void* Q, const void* K, const void* V,
@@ -218,6 +223,41 @@ dit_status_t attn_patch_fwd_ws(const void* Q_p, const void* K_p, const void* V_p
                                dit_dtype_t in_dtype, dit_dtype_t out_dtype,
                                void* workspace, long long workspace_bytes,
                                hipStream_t stream);
+
+/*
+ * PipeFusion patch step for a patch made of several evenly spaced runs of
+ * buffer rows.  The pages split the image into patches (xDiT abstract) of
+ * possibly unequal size (Orchestra, abstract) without fixing their shape; a
+ * band of spatial rows across every frame of a video is, in frame-major
+ * token order, one run of rows per frame:
+ *   run r (0 <= r < n_runs) covers buffer rows
+ *       [p0 + r * run_stride, p0 + r * run_stride + run_len),
+ *   and the patch tensors hold the runs back to back (Np = n_runs * run_len
+ *   rows; patch row r * run_len + i is buffer row p0 + r * run_stride + i).
+ *   K_buf/V_buf: every run's rows <- the run's rows of K_p/V_p (bit copy);
+ *   then (O, LSE) <- attn_block_fwd(Q_p, K_buf, V_buf) over all N rows.
+ *   Q_p, K_p, V_p: [B,H,Np,d] in_dtype                 (read only)
+ *   K_buf, V_buf:  [B,H,N,d] in_dtype                  (the runs' rows overwritten)
+ *   O: [B,H,Np,d] out_dtype; LSE: [B,H,Np] float32     (written)
+ *   run_len >= 1, n_runs >= 1, p0 >= 0; with n_runs > 1, run_stride >=
+ *   run_len (runs in order, never overlapping; run_stride is not used when
+ *   n_runs == 1); p0 + (n_runs - 1) * run_stride + run_len <= N; otherwise
+ *   DIT_ERR_INVALID_ARG.
+ *   workspace: NULL for the plain launch, or as for attn_patch_fwd_ws (at
+ *   least attn_block_workspace_bytes(B, H, Np, N, d) bytes, zero-filled
+ *   before its first use).
+ * With n_runs == 1 this is attn_patch_fwd (workspace NULL) or
+ * attn_patch_fwd_ws with Np = run_len.  Buffers and overlap rules as
+ * attn_patch_fwd.
+ */
+dit_status_t attn_patch_fwd_strided(const void* Q_p, const void* K_p, const void* V_p,
+                                    void* K_buf, void* V_buf,
+                                    void* O, float* LSE,
+                                    int B, int H, int run_len, int n_runs, int run_stride,
+                                    int N, int p0, int d, float scale,
+                                    dit_dtype_t in_dtype, dit_dtype_t out_dtype,
+                                    void* workspace, long long workspace_bytes,
+                                    hipStream_t stream);
 
 /*
  * Classifier-free guidance combine of the unconditional and conditional

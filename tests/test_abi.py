@@ -29,6 +29,17 @@ def ptr(i, off=0):
     return BASE + i * GAP + off
 
 
+SPLIT_RECORD_BYTES = 256 + 4 * 256 * (128 + 1) * 4
+
+
+def split_ws_bytes(B, H, Nq, d):
+    """One fixed record per 256-row query tile, whatever the head dim: a
+    counter in the first 256 bytes, then four fp32 partials of 256 rows x
+    (128 + 1) floats."""
+    items = B * H * ((Nq + 255) // 256)
+    return items * SPLIT_RECORD_BYTES
+
+
 @pytest.fixture(scope="module")
 def lib():
     return binding.load()
@@ -146,6 +157,51 @@ def test_attn_patch_fwd_rejects(lib, kw, code):
 
 
 # ---------------------------------------------------------------------------
+# attn_patch_fwd_strided
+# ---------------------------------------------------------------------------
+
+def strided(lib, **kw):
+    a = dict(Q=ptr(0), Kp=ptr(1), Vp=ptr(2), Kb=ptr(3), Vb=ptr(4), O=ptr(5), L=ptr(6), B=1, H=4,
+             run_len=64, n_runs=8, stride=512, N=4096, p0=64, d=128, scale=0.088, i=BF16, o=BF16,
+             W=None, nbytes=0)
+    a.update(kw)
+    return lib.attn_patch_fwd_strided(a["Q"], a["Kp"], a["Vp"], a["Kb"], a["Vb"], a["O"], a["L"],
+                                      a["B"], a["H"], a["run_len"], a["n_runs"], a["stride"],
+                                      a["N"], a["p0"], a["d"], a["scale"], a["i"], a["o"], a["W"],
+                                      a["nbytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), INV), (dict(Kp=None), INV), (dict(Vb=None), INV), (dict(L=None), INV),
+    (dict(run_len=0), INV), (dict(run_len=-4), INV), (dict(n_runs=0), INV), (dict(N=0), INV),
+    (dict(p0=-1), INV),
+    (dict(stride=63), INV),                      # runs overlap
+    (dict(stride=-512), INV),                    # runs backwards
+    (dict(p0=449), INV),                         # last run ends one row past the buffer
+    (dict(n_runs=9), INV),                       # a ninth run does not fit
+    (dict(run_len=1 << 16, n_runs=1 << 15, stride=1 << 16, N=(1 << 31) - 1, p0=0), INV),  # ends at 2^31
+    (dict(d=100), UNS), (dict(i=F32, o=BF16), UNS), (dict(scale=math.inf), INV),
+    (dict(Kp=ptr(3, 4096)), INV),                # fresh patch inside the buffer
+    (dict(O=ptr(4, 128)), INV),                  # output inside the V buffer
+    (dict(W=ptr(7)), INV),                       # workspace of 0 bytes
+    (dict(W=ptr(7, 16), nbytes=split_ws_bytes(1, 4, 512, 128)), INV),   # misaligned workspace
+    (dict(W=ptr(3), nbytes=split_ws_bytes(1, 4, 512, 128)), INV),       # workspace is K_buf
+])
+def test_attn_patch_fwd_strided_rejects(lib, kw, code):
+    assert strided(lib, **kw) == code
+
+
+def test_attn_patch_fwd_strided_edge_layouts_pass_validation(lib):
+    """Layouts at the limits are accepted by the checks: the call then reaches
+    the HIP runtime, which fails here without a GPU (DIT_ERR_HIP), not the
+    validation codes.  One run ignores the stride; touching runs (stride ==
+    run_len) and a last run ending exactly at N are allowed."""
+    for kw in (dict(n_runs=1, stride=0, run_len=512), dict(stride=64),
+               dict(p0=448), dict(B=1, H=70000, run_len=1, n_runs=1, N=2, p0=1, d=8)):
+        assert strided(lib, **kw) == HIP, kw
+
+
+# ---------------------------------------------------------------------------
 # cfg_combine
 # ---------------------------------------------------------------------------
 
@@ -193,18 +249,19 @@ def test_attn_block_fwd_merge_rejects(lib, kw, code):
 # attn_block_fwd_ws (split launch with a caller workspace)
 # ---------------------------------------------------------------------------
 
-def split_ws_bytes(B, H, Nq, d):
-    """Counters (uint32 per 256-row query tile, padded to 256 B), then four fp32
-    partials (256 rows x (d + 1) floats) per query tile."""
-    items = B * H * ((Nq + 255) // 256)
-    return (items * 4 + 255) // 256 * 256 + items * 4 * 256 * (d + 1) * 4
-
-
 @pytest.mark.parametrize("shape", [(1, 24, 2048, 2048, 128), (2, 16, 4096, 4096, 72),
                                    (1, 1, 1, 1, 8), (3, 5, 257, 9, 64)])
 def test_block_workspace_bytes(lib, shape):
     B, H, Nq, Nkv, d = shape
     assert lib.attn_block_workspace_bytes(B, H, Nq, Nkv, d) == split_ws_bytes(B, H, Nq, d)
+
+
+def test_block_workspace_records_do_not_depend_on_the_head_dim(lib):
+    """A counter sits at the start of its tile's record for every shape, so the
+    counters of one call never fall inside another call's partial slots."""
+    sizes = {lib.attn_block_workspace_bytes(1, 24, 2048, 2048, d) for d in range(8, 129, 8)}
+    assert sizes == {192 * SPLIT_RECORD_BYTES}
+    assert lib.attn_block_workspace_bytes(1, 24, 1024, 2048, 64) == 96 * SPLIT_RECORD_BYTES
 
 
 def test_block_workspace_bytes_invalid(lib):

@@ -29,9 +29,14 @@ def dev(t):
     return t.to("cuda:0")
 
 
+RECORD_BYTES = 256 + 4 * 256 * (128 + 1) * 4   # one workspace record per 256-row query tile
+
+
 def counters_zero(ws, B, H, Nq):
+    """The arrival counters (first word of each tile's record) are all zero."""
     items = B * H * ((Nq + 255) // 256)
-    return int(ws[: items * 4].view(torch.int32).abs().sum().item()) == 0
+    words = ws[: items * RECORD_BYTES].view(items, RECORD_BYTES)[:, :4].contiguous().view(torch.int32)
+    return int(words.abs().sum().item()) == 0
 
 
 # Shapes whose plain grid (one 256-row query tile per workgroup) leaves part of
@@ -221,6 +226,30 @@ def test_workspace_reused_by_a_smaller_call():
     Or, Lr = oracle.ref_attn(to_oracle(q2), to_oracle(k2), to_oracle(v2), inputs.default_scale(128))
     assert_bf16_close(to_f64(O), Or, "reuse O")
     assert_bf16_close(to_f64(L), Lr, "reuse LSE")
+
+
+def test_workspace_reused_across_tile_counts_and_head_dims():
+    """One workspace, made for the largest call, serves in turn: 384 query
+    tiles at d128, then 192 tiles at d64 (fewer counters, other partial
+    sizes), then 384 tiles at d128 again, all through forced splits.  Each
+    result against the oracle, every counter back at zero after each call."""
+    shapes = [(1, 24, 4096, 700, 128), (1, 24, 2048, 700, 64), (1, 24, 4096, 700, 128)]
+    big = inputs.attn_inputs(*shapes[0][:4], shapes[0][4], "bf16", seed=31)
+    ws = attn_block_workspace(dev(big[0]), dev(big[1]))
+    for n, (B, H, Nq, Nkv, d) in enumerate(shapes):
+        q, k, v = inputs.attn_inputs(B, H, Nq, Nkv, d, "bf16", seed=31 + n)
+        scale = inputs.default_scale(d)
+        say("case workspace reuse", n, (B, H, Nq, Nkv, d))
+        qd, kd, vd = dev(q), dev(k), dev(v)
+        O, L = attn_block_fwd(qd, kd, vd, scale=scale, out_dtype=torch.float32, workspace=ws,
+                              force_split=True)
+        Op, Lp = attn_block_fwd(qd, kd, vd, scale=scale, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert not (torch.equal(O, Op) and torch.equal(L, Lp)), "split launch was not taken"
+        assert counters_zero(ws, 1, 24, 4096), f"counters not all zero after call {n}"
+        Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale)
+        assert_bf16_close(to_f64(O), Or, f"reuse {n} O")
+        assert_bf16_close(to_f64(L), Lr, f"reuse {n} LSE")
 
 
 def test_fp32_inputs_ignore_the_workspace():
