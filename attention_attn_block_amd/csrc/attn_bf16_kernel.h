@@ -693,9 +693,19 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       // partials take one representation -- O normalised, in fp32, and LSE in
       // log2 units -- and are combined in key order, so the result is the same
       // bits whichever piece combines.
-      constexpr int kSlot = kRowsWG * (D + 1);  // floats per partial: O rows, then LSE
-      static_assert(kSlot * 4 <= kAttnSplitSlotBytes, "a partial must fit its workspace slot");
+      // A partial is stored in the accumulators' own lane order, so that every
+      // store and load of the exchange moves 1 KB of contiguous memory: O in
+      // 1 KB units ((wave * NG + g) * kDTiles + dt) * 4 + q4, lane l at byte
+      // 16 l of its unit, holding row (wave * NG + g) * 32 + l % 32 and
+      // columns dt * 32 + 8 q4 + 4 (l / 32) .. +3 (units past d are never
+      // written or read); then the LSE of row r at byte kOBytes + 4 r.
+      constexpr int kOBytes = (kThreads / 64) * NG * G::kDTiles * 4 * 1024;
+      constexpr int kSlotBytes = kOBytes + kRowsWG * 4;
+      static_assert(kSlotBytes <= kAttnSplitSlotBytes, "a partial must fit its workspace slot");
       constexpr long long kSlotStride = kAttnSplitSlotBytes / 4;  // floats between slots
+      auto o_off = [&](int g, int dt, int q4) {
+        return ((((wave * NG + g) * G::kDTiles + dt) * 4 + q4) * 64 + lane) * 16;
+      };
       const long long total = (long long)n_items * n_all;
       // Workgroup whose range holds unit x (ranges start at total * w / nblk).
       auto owner = [&](long long x) { return ((x + 1) * nblk + total - 1) / total - 1; };
@@ -723,7 +733,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       // reusing from L2.
       auto slot_rsrc = [&](int j) {
         return __builtin_amdgcn_make_buffer_rsrc(slots + (size_t)j * kSlotStride, (short)0,
-                                                 kSlot * 4, kBufferFlags);
+                                                 kSlotBytes, kBufferFlags);
       };
       constexpr int kCoherent = 16;  // sc1
       auto publish = [&]() {
@@ -741,11 +751,11 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(u32x4, f32x4{acc[g][dt][4 * q4], acc[g][dt][4 * q4 + 1],
                                                     acc[g][dt][4 * q4 + 2], acc[g][dt][4 * q4 + 3]}),
-                    own, (row * D + d0) * 4, 0, kCoherent);
+                    own, o_off(g, dt, q4), 0, kCoherent);
             }
           if (hi == 0)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse_own[g]), own,
-                                                  (kRowsWG * D + row) * 4, 0, kCoherent);
+                                                  kOBytes + row * 4, 0, kCoherent);
         }
       };
       // Arrival on the tile's counter (0 before the first piece arrives; the
@@ -802,7 +812,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 #pragma unroll
           for (int j = 0; j < kMaxPieces; ++j)
             lp[j] = j < n_pieces ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                       slot_rsrc(j), (kRowsWG * D + row) * 4, 0, kCoherent))
+                                       slot_rsrc(j), kOBytes + row * 4, 0, kCoherent))
                                  : 0.f;
           float m = -INFINITY;
 #pragma unroll
@@ -849,7 +859,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
                   const int d0 = dt * 32 + 8 * q4 + 4 * hi;
                   pv[i][q4] = d0 < D
                                   ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                        slot_rsrc(i + (i >= j_piece)), (row * D + d0) * 4, 0, kCoherent))
+                                        slot_rsrc(i + (i >= j_piece)), o_off(g, dt, q4), 0, kCoherent))
                                   : f32x4{};
                 }
               } else {
