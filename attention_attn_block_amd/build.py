@@ -1,7 +1,9 @@
 """Build libdit_attn.so in-tree for gfx950 with hipcc.
 
 Each ``csrc/*.hip`` file compiles to an object in ``_build/`` (in parallel),
-then one shared library is linked next to this file.  The plain-C client of
+then one shared library is linked next to this file.  The measured-peak
+micro-benchmarks in ``csrc/peaks/`` become a second library,
+``libdit_peaks.so``, used only by the benchmark.  The plain-C client of
 the ABI in ``tests/abi_client.c`` is then compiled with the host C compiler
 and linked against that library.  Always recompiles.
 
@@ -19,6 +21,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdit_attn.so")
+PEAKS_SRC = os.path.join(CSRC, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(HERE, "libdit_peaks.so")
 ARCH = "gfx950"
 CLIENT_SRC = os.path.join(ROOT, "tests", "abi_client.c")
 CLIENT = os.path.join(ROOT, "tests", "abi_client")
@@ -53,11 +57,14 @@ def build(verbose=False, jobs=None):
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
     objs = [os.path.join(BUILD, f[:-4] + ".o") for f in srcs]
     cmds = [[cc, *FLAGS, "-I", CSRC, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
+    # The measured-peak micro-benchmarks: a library of their own, for the benchmark.
+    cmds.append([cc, *FLAGS, "-shared", PEAKS_SRC, "-o", PEAKS_LIB + ".tmp"])
     jobs = jobs or min(len(cmds), max(1, os.cpu_count() or 1))
     with cf.ThreadPoolExecutor(jobs) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
+    os.replace(PEAKS_LIB + ".tmp", PEAKS_LIB)
     tmp = LIB + ".tmp"
     _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     os.replace(tmp, LIB)

@@ -19,12 +19,20 @@ dominant kernel and the fp64 CPU oracle on a bounded sample ride along.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--no-cpu-baseline]
 
-The default warm-up (about 0.7 s of steps) lets the shader clock settle at its
-steady value under this load before timing; the clock and board power sampled
-during the timed steps are reported (clock_during_timed_steps).
+The shader clock needs about half a second of this load to settle at its
+steady value; the supplementary workloads (merge and CFG on cold HBM, other
+per-device shapes, d = 72 attention) run first, before the warm-up steps, so
+the timed steps see the steady-state clock of a GPU under continuous load
+(also with a short --warmup).  --no-supplementary skips them.
+
+Phase figures time groups of back-to-back calls between two events, so no
+event sits between two kernels of a group; measured peaks of the same GPU (a
+matrix-core loop and a streaming copy, libdit_peaks.so) are reported beside
+the published ones.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -41,6 +49,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "attn_fwd_bf16_d128_video_patch_traffic.txt")
 ATTN_SRC = os.path.join(ROOT, "attention_attn_block_amd", "csrc", "attn_bf16_kernel.h")
+PEAKS_LIB = os.path.join(ROOT, "attention_attn_block_amd", "libdit_peaks.so")
 
 
 def parse():
@@ -71,10 +80,23 @@ def kernel_traffic():
     return float(m_b.group(1)) if sha == m_sha.group(1) else None
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w_patch):
     """fp64 oracle on a bounded sample of the dominant phase: all 24 heads of
     the PipeFusion patch attention, 4096 query rows each, over the full
-    32768-row buffer (the splice is a copy and is left out)."""
+    32768-row buffer (the splice is a copy and is left out).  The oracle's
+    BLAS runs on every core this process may use (its affinity set)."""
     import numpy as np
     import threadpoolctl
 
@@ -85,15 +107,72 @@ def cpu_baseline(w_patch):
     q, kb, vb = to_oracle(w_patch["q_p"]), to_oracle(w_patch["k_buf"]), to_oracle(w_patch["v_buf"])
     B, H, _, d = q.shape
     N = kb.shape[2]
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    t0 = time.perf_counter()
-    oracle.ref_attn(q, kb, vb, w_patch["scale"], rows=rows)
-    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    with threadpoolctl.threadpool_limits(limits=cores, user_api="blas"):
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+        t0 = time.perf_counter()
+        oracle.ref_attn(q, kb, vb, w_patch["scale"], rows=rows)
+        dt = time.perf_counter() - t0
     flops = attn_flops(B, H, rows.size, N, d)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle attention, B{B} H{H}, {rows.size} of 8192 patch query rows "
-                      f"against the full {N}-row buffer, d{d}: {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "blas_threads": int(threads), "cpu_model": cpu_model(),
+            "sample": f"fp64 oracle attention (numpy, BLAS on {threads} threads), B{B} H{H}, "
+                      f"{rows.size} of 8192 patch query rows against the full {N}-row buffer, "
+                      f"d{d}: {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+
+
+def measured_peaks(torch, dev):
+    """Peaks of this GPU measured by libdit_peaks.so: a bf16 matrix-core loop
+    (no memory traffic; 2 workgroups of 8 waves per CU) and a streaming copy
+    of 1 GiB (read + write counted).  Each is timed over back-to-back
+    launches after a warm-up; None if the library is not built."""
+    if not os.path.exists(PEAKS_LIB):
+        return None
+    L = ctypes.CDLL(PEAKS_LIB)
+    L.dit_peak_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.dit_peak_mfma_flops.restype = ctypes.c_double
+    L.dit_peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.dit_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    wgs, iters = 2 * n_cu, 2000
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+
+    def run_timed(fn, warm, reps):
+        for _ in range(warm):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps   # s per launch
+
+    def mfma():
+        assert L.dit_peak_mfma_bf16(wgs, iters, ctypes.c_void_p(sink.data_ptr()), stream) == 0
+
+    t_mfma = run_timed(mfma, 100, 100)
+    flops = L.dit_peak_mfma_flops(wgs, iters)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    copy_gbs = {}
+    for unroll in (1, 2, 4):
+        def copy():
+            assert L.dit_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                   nbytes, unroll, stream) == 0
+        copy_gbs[unroll] = 2 * nbytes / run_timed(copy, 5, 20) / 1e9
+    del src, dst, sink
+    return {"mfma_bf16_tflops": flops / t_mfma / 1e12, "hbm_copy_gbs": max(copy_gbs.values()),
+            "hbm_copy_gbs_by_unroll": copy_gbs,
+            "note": f"matrix-core loop: {wgs} workgroups x 8 waves x {4 * iters} rounds of 4 "
+                    "independent 32x32x16 bf16 products, 100 launches after 100; copy: 1 GiB, "
+                    "16-byte non-temporal, 1, 2 or 4 units per lane (best kept), read + write "
+                    "bytes, 20 launches after 5 each"}
 
 
 def main():
@@ -184,6 +263,13 @@ def main():
         cfg_combine(eps_u, eps_c, s_cfg, out=eps_out)
         rec()
 
+    # ---- supplementary and measured peaks, before the warm-up (they also bring
+    # the shader clock to its steady state under load) ------------------------------
+    supp, peaks = {}, None
+    if not args.no_supplementary:
+        peaks = measured_peaks(torch, dev)
+        supp = supplementary(torch, dev, inputs, q_r, ks, vs, wr["scale"])
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -192,61 +278,86 @@ def main():
     pevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    sampler = ClockSampler()
-    sampler.start()
     t_start.record()
     for k in range(args.steps):
         step(patch_ev=pevs[k])
     t_end.record()
     torch.cuda.synchronize()
-    clock = sampler.stop()
     ms_step = t_start.elapsed_time(t_end) / args.steps
     patch_ms = [a.elapsed_time(b) for a, b in pevs]
 
-    # ---- phase breakdown: instrumented steps after the timed region --------------
+    # ---- phase breakdown, after the timed region ---------------------------------
+    # The ring share again with each block's partial in a buffer of its own: the
+    # 8 block calls run back to back between two events, then the 7 merges
+    # (folding blocks 1..7 into block 0's partial, in order) between two more,
+    # so no event sits between two kernels of a group.  The per-call event
+    # figures of the in-sequence step are kept for comparison (an event pair
+    # around each ~14 us merge adds its own overhead).
     n_phase = 10
+    parts = [(torch.empty_like(o_acc), torch.empty_like(l_acc)) for _ in range(nblk)]
+    grp = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_phase)]
+    cfg_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_phase)]
+    for k in range(n_phase):
+        grp[k][0].record()
+        for j in range(nblk):
+            attn_block_fwd(q_r, ks[j], vs[j], scale=wr["scale"], out_dtype=torch.float32,
+                           out=parts[j][0], lse=parts[j][1])
+        grp[k][1].record()
+        grp[k][2].record()
+        for j in range(1, nblk):
+            attn_lse_merge(parts[0][0], parts[0][1], parts[j][0], parts[j][1])
+        grp[k][3].record()
+        cfg_ev[k][0].record()
+        for _ in range(10):
+            cfg_combine(eps_u, eps_c, s_cfg, out=eps_out)
+        cfg_ev[k][1].record()
+    torch.cuda.synchronize()
+    ring_ms = [e[0].elapsed_time(e[1]) / nblk for e in grp]
+    merge_ms = [e[2].elapsed_time(e[3]) / (nblk - 1) for e in grp]
+    cfg_ms = [e[0].elapsed_time(e[1]) / 10 for e in cfg_ev]
+    del parts
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(n_phase)]
     for k in range(n_phase):
         step(evs[k])
     torch.cuda.synchronize()
-    ring_ms, merge_ms, cfg_ms = [], [], []
+    merge_seq_ms = []
     for ev in evs:
         i = 0
         for j in range(nblk):
-            ring_ms.append(ev[i].elapsed_time(ev[i + 1]))
             i += 2
             if j:
-                merge_ms.append(ev[i].elapsed_time(ev[i + 1]))
+                merge_seq_ms.append(ev[i].elapsed_time(ev[i + 1]))
                 i += 2
-        i += 2
-        cfg_ms.append(ev[i].elapsed_time(ev[i + 1]))
 
     def mean(x):
         return sum(x) / len(x)
 
-    ring_us, merge_us, patch_us, cfg_us = (1e3 * mean(x) for x in (ring_ms, merge_ms, patch_ms, cfg_ms))
+    ring_us, merge_us, patch_us, cfg_us, merge_seq_us = (
+        1e3 * mean(x) for x in (ring_ms, merge_ms, patch_ms, cfg_ms, merge_seq_ms))
     f_block = attn_flops(Br, Hr, Nqr, Nkr, dr)
     patch_tflops = f_patch / (patch_us * 1e-6) / 1e12
     phases = {
-        "note": f"ring, merge and CFG per call from {n_phase} instrumented steps after the timed region",
+        "note": f"means over {n_phase} repetitions after the timed region; ring blocks, merges "
+                "and CFG each timed as a group of back-to-back calls between two events",
         "ring_block_attn": {"us_per_call": ring_us, "calls_per_step": nblk,
                             "tflops": f_block / (ring_us * 1e-6) / 1e12,
-                            "frac_bf16_peak": f_block / (ring_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS},
-        "lse_merge_in_sequence": {"us_per_call": merge_us, "calls_per_step": nblk - 1,
-                                  "gbs": merge_bytes / (merge_us * 1e-6) / 1e9,
-                                  "frac_hbm_peak": merge_bytes / (merge_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                                  "note": "cache-warm: O_b was just written by the block call"},
+                            "frac_bf16_peak": f_block / (ring_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                            "note": "8 block calls back to back, fp32 partials"},
+        "lse_merge": {"us_per_call": merge_us, "calls_per_step": nblk - 1,
+                      "gbs": merge_bytes / (merge_us * 1e-6) / 1e9,
+                      "frac_hbm_peak": merge_bytes / (merge_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                      "note": "7 merges back to back, folding the 8 block partials in order"},
+        "lse_merge_in_sequence_events": {
+            "us_per_call": merge_seq_us, "gbs": merge_bytes / (merge_seq_us * 1e-6) / 1e9,
+            "frac_hbm_peak": merge_bytes / (merge_seq_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "note": "each merge of the step bracketed by its own event pair (O_b just written "
+                    "by the block call); includes the events' own overhead"},
         "patch_splice_plus_attn": {"us_per_call": patch_us, "tflops": patch_tflops,
                                    "frac_bf16_peak": patch_tflops / PEAK_BF16_TFLOPS,
                                    "note": "events around this call in every timed step"},
         "cfg_combine": {"us_per_call": cfg_us, "gbs": cfg_bytes / (cfg_us * 1e-6) / 1e9,
-                        "note": "96 KiB working set: launch-latency bound"},
+                        "note": "96 KiB working set, 10 calls back to back: launch-latency bound"},
     }
-
-    # ---- supplementary, outside the timed region ---------------------------------
-    supp = {}
-    if not args.no_supplementary:
-        supp = supplementary(torch, dev, inputs, q_r, ks, vs, wr["scale"])
 
     roofline = {"bound": "mfma", "achieved": patch_tflops, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": patch_tflops / PEAK_BF16_TFLOPS,
@@ -254,6 +365,13 @@ def main():
                 "kernel": "attn_fwd_bf16_kernel<128, bf16 out> in attn_patch_fwd "
                           "(8192 queries x 32768 keys x 24 heads; timed with the splice "
                           "that precedes it in the same call)"}
+    if peaks:
+        roofline["measured_peak"] = peaks["mfma_bf16_tflops"]
+        roofline["frac_of_measured_peak"] = patch_tflops / peaks["mfma_bf16_tflops"]
+        for name, unit in (("ring_block_attn", "tflops"), ("lse_merge", "gbs"),
+                           ("lse_merge_in_sequence_events", "gbs"), ("patch_splice_plus_attn", "tflops")):
+            peak = peaks["mfma_bf16_tflops"] if unit == "tflops" else peaks["hbm_copy_gbs"]
+            phases[name]["frac_of_measured_peak"] = phases[name][unit] / peak
 
     value = f_step / (ms_step * 1e-3) / 1e12
     out = {
@@ -268,72 +386,12 @@ def main():
                    "attn_flops_per_step": f_step, "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
         "roofline": roofline,
         "phases": phases,
-        "clock_during_timed_steps": clock,
+        "measured_peaks": peaks,
         "supplementary": supp,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wp)
     print(json.dumps(out), flush=True)
-
-
-class ClockSampler:
-    """Samples the GPU's current shader clock (pp_dpm_sclk, the level marked
-    '*') and board power (hwmon power1_input) from sysfs every 20 ms on a
-    background thread, for the timed region only.  Reports null where the
-    files do not exist."""
-
-    def __init__(self):
-        import glob
-        import threading
-        self.samples = []
-        self.path = None
-        for dev_dir in sorted(glob.glob("/sys/class/drm/card*/device")):
-            if os.path.exists(os.path.join(dev_dir, "pp_dpm_sclk")):
-                self.path = dev_dir
-                break
-        self.power = None
-        if self.path:
-            hw = sorted(glob.glob(os.path.join(self.path, "hwmon", "*", "power1_input")))
-            self.power = hw[0] if hw else None
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-
-    def _read(self):
-        with open(os.path.join(self.path, "pp_dpm_sclk")) as f:
-            m = re.search(r"(\d+)\s*Mhz\s*\*", f.read())
-        w = None
-        if self.power:
-            with open(self.power) as f:
-                w = int(f.read().strip()) / 1e6
-        return (int(m.group(1)) if m else None, w)
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                self.samples.append(self._read())
-            except (OSError, ValueError):
-                return
-            time.sleep(0.02)
-
-    def start(self):
-        if self.path:
-            self._thread.start()
-
-    def stop(self):
-        if not self.path:
-            return None
-        self._stop.set()
-        self._thread.join()
-        clk = sorted(c for c, _ in self.samples if c)
-        pw = sorted(w for _, w in self.samples if w is not None)
-        if not clk:
-            return None
-
-        def q(a, f):
-            return a[int(f * (len(a) - 1))] if a else None
-        return {"sclk_mhz_median": q(clk, 0.5), "sclk_mhz_p10": q(clk, 0.1),
-                "sclk_mhz_p90": q(clk, 0.9), "power_w_median": q(pw, 0.5),
-                "samples": len(clk), "source": "sysfs pp_dpm_sclk / hwmon power1_input, 20 ms"}
 
 
 def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):

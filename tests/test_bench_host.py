@@ -1,6 +1,7 @@
 """Host-side pieces of bench.py on the CPU: the roofline's traffic figure is
 read from a counter summary only when that summary names the current kernel
-source, and the clock sampler degrades to null without the sysfs files."""
+source; the CPU model is read from the host; the measured peaks are null
+without their library."""
 
 import hashlib
 import os
@@ -33,11 +34,11 @@ def test_traffic_only_for_the_current_source(tmp_path, monkeypatch):
     assert bench.kernel_traffic() is None                 # no source hash
 
 
-def test_clock_sampler_without_sysfs(monkeypatch):
-    s = bench.ClockSampler()
-    s.path = None
-    s.start()
-    assert s.stop() is None
+def test_cpu_model_and_peaks_without_library(monkeypatch, tmp_path):
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
+    monkeypatch.setattr(bench, "PEAKS_LIB", str(tmp_path / "missing.so"))
+    assert bench.measured_peaks(None, None) is None
 
 
 def test_attn_flops():
