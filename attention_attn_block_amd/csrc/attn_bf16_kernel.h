@@ -224,8 +224,22 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // swz_k / swz_v), plus slack for the transposing reads of the last rows.
   constexpr int kTileUnits = kBc * G::kOct;
   constexpr int kBufUnits = kTileUnits + 16;
-  __shared__ u32x4 k_lds[2][kBufUnits];
-  __shared__ u32x4 v_lds[2][kBufUnits];
+  // Ones row.  When d is not a multiple of 32 the PV product computes
+  // padding rows of O^T (d pads to 32 kDTiles); the transposing V reads of
+  // those rows are pointed at a region of bf16 ones, so each padding row of
+  // O^T accumulates the row sum of the weights: the normaliser comes out of
+  // the matrix cores, and the vector phase needs no sums (see kFastNorm).
+  // The region lies past the four tile buffers and is sized so that the
+  // address of every padding read -- a fixed offset of two buffers plus
+  // kOnesSkew units from either V buffer, plus the chunk and half-chunk
+  // offsets -- lands in it.  The skew moves the padding reads to other banks
+  // than the real V reads of the same pass (none conflict at d = 72).
+  constexpr bool kOnesRow = (D % 32) != 0;
+  constexpr int kOnesSkew = 8;
+  constexpr int kOnesUnits = kOnesRow ? kBufUnits + kOnesSkew + 56 * G::kOct + 1 : 0;
+  __shared__ u32x4 lds_all[4 * kBufUnits + kOnesUnits];
+  u32x4 (*const k_lds)[kBufUnits] = reinterpret_cast<u32x4 (*)[kBufUnits]>(lds_all);
+  u32x4 (*const v_lds)[kBufUnits] = k_lds + 2;
   __shared__ unsigned s_arrive;  // SPLIT: counter value seen by this workgroup
 
   const int tid = threadIdx.x;
@@ -316,6 +330,13 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 #pragma unroll
   for (int c = 0; c < G::kChunks; ++c) k_unit[c] = l32 * G::kOct + (((2 * c + hi) ^ sk) % G::kOct);
 
+  if constexpr (kOnesRow) {
+    // Written once; no tile load ever touches this region.  The first piece's
+    // prologue barrier orders these stores before any read.
+    const u32x4 one4 = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    for (int i = tid; i < kOnesUnits; i += kThreads) lds_all[4 * kBufUnits + i] = one4;
+  }
+
   while (u < u_end) {
     // One piece: key tiles [t_beg, t_end) of query tile `item`.
     const int item = (int)(u / n_all);
@@ -396,21 +417,25 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 #pragma unroll
     for (int dt = 0; dt < G::kDTiles; ++dt) {
       const int unit = 4 * dt + 2 * (vq & 1) + ((vi & 3) >> 1);
-      // d = 72: the reads past the last unit (output rows never stored) take
-      // unit 8 of the same row, a broadcast.
-      const int slot = G::kOct == 9 ? v9_slot(v_row & 3, unit < 9 ? unit : 8) : (unit ^ sv);
+      if (kOnesRow && unit >= G::kOct) {
+        // A padding row of O^T: read the ones region (two buffers and
+        // kOnesSkew units past this V buffer, whichever it is; see kOnesUnits).
+        v_off[dt] = (2 * kBufUnits + kOnesSkew) * 8 + 4 * (vi & 1);
+        continue;
+      }
+      const int slot = G::kOct == 9 ? v9_slot(v_row & 3, unit) : (unit ^ sv);
       v_off[dt] = (v_row * G::kOct + slot) * 8 + 4 * (vi & 1);
     }
 
     f32x16 acc[NG][G::kDTiles];
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int t = 0; t < G::kDTiles; ++t) acc[g][t] = f32x16{};
     float l_run[NG];   // this lane's share of each row's normaliser (bf16 weights)
     float m_ref[NG];   // reference row max for the exponentials, log2 units
+    float l_fin[NG];   // each row's normaliser at the end of the key loop
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
     const int n_tiles = t_end - t_beg;  // key tiles of this piece
+    // Accumulator element of a lane that holds a padding row of O^T (row
+    // 32 (kDTiles - 1) + 8 (e / 4) + 4 hi + e % 4 >= d for both half-waves).
+    constexpr int kOnesElt = 4 * ((D - 32 * (G::kDTiles - 1)) / 8);
 
     // Ping-pong schedule.  Waves w and w + 4 share a SIMD.  Group A (waves 0-3)
     // and group B (waves 4-7) run the same per-wave pipeline one slot apart, so
@@ -427,23 +452,15 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     // in slot 2k-1.  Slot 2k+1 ends by waiting for both (the barrier of slot
     // 2k does not wait).
     const int grp = wave >> 2;
-    if (grp == 1) {
-      dma_tile(IsK{}, Kh, k_lds[0], kvb);
-      dma_tile(IsV{}, Vh, v_lds[0], kvb);
-      if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kvb + kBc);
-    }
-    dma_wait();
-    __syncthreads();
-
     f32x16 s_nxt[NG][kKT];
     bf16x8 pb[NG][kCH];
-    qk(0, s_nxt);
-    // Slot 0 loads K tile 2 into the buffer tile 0 was just read from: every
-    // wave must have finished those reads first.
-    __syncthreads();
 
     // W(t): scores of tile t (raw, in s_nxt) -> weights pb, normaliser share.
-    auto w_phase = [&](int t) __attribute__((always_inline)) {
+    // kSafe = false (ones-row head dims only): the weights alone; the
+    // normaliser comes out of the PV product and nothing bounds the weights
+    // per tile (checked once after the key loop).
+    auto w_phase = [&](auto safe_c, int t) __attribute__((always_inline)) {
+      constexpr bool kSafe = decltype(safe_c)::value;
       mask_tail(s_nxt, kvb + t * kBc);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
@@ -456,6 +473,16 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
         for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s_nxt[g][kt][r] = fmaf(s_nxt[g][kt][r], c2, neg_m);
+      }
+      if constexpr (!kSafe) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int ch = 0; ch < kCH; ++ch)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              pb[g][ch][j] = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
+        return;
       }
       float ls[NG];
 #pragma unroll
@@ -578,7 +605,27 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       __builtin_amdgcn_s_setprio(0);
     };
 
-    w_phase(0);
+    // The whole key loop of the piece: prologue, then the slots.  Leaves the
+    // piece's (acc, m_ref, l_fin).
+    auto pipeline = [&](auto safe_c) __attribute__((always_inline)) {
+    constexpr bool kSafe = decltype(safe_c)::value;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int t = 0; t < G::kDTiles; ++t) acc[g][t] = f32x16{};
+    if (grp == 1) {
+      dma_tile(IsK{}, Kh, k_lds[0], kvb);
+      dma_tile(IsV{}, Vh, v_lds[0], kvb);
+      if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kvb + kBc);
+    }
+    dma_wait();
+    __syncthreads();
+    qk(0, s_nxt);
+    // Slot 0 loads K tile 2 into the buffer tile 0 was just read from: every
+    // wave must have finished those reads first.
+    __syncthreads();
+
+    w_phase(safe_c, 0);
 
     // One slot; p = slot index mod 4 (compile-time), so the buffer of every
     // tile a slot touches is known: in slots 4j + {0, 1} tile k is even, in
@@ -596,12 +643,12 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
         if (grp == 0) {
           if (k < n_tiles) m_phase(KQ{}, KP{}, k);
         } else {
-          if (k >= 1 && k < n_tiles) w_phase(k);
+          if (k >= 1 && k < n_tiles) w_phase(safe_c, k);
         }
       } else {
         if (grp == 0) {  // group A is in its vector phase in odd slots
           if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], kvb + (k + 1) * kBc);
-          if (k + 1 < n_tiles) w_phase(k + 1);
+          if (k + 1 < n_tiles) w_phase(safe_c, k + 1);
         } else {
           if (k < n_tiles) m_phase(KQ{}, KP{}, k);
         }
@@ -629,11 +676,31 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       run_slot(P2{}, s + 2);
       run_slot(P3{}, s + 3);
     }
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      l_fin[g] = kSafe ? sum_with_partner32(l_run[g]) : acc[g][G::kDTiles - 1][kOnesElt];
+    };  // pipeline
+
+    if constexpr (kOnesRow) {
+      // Fast path first.  Its weights are exp2 of (score - reference max of
+      // the first tile) with no bound: a row whose scores later outgrow that
+      // reference by 128 (log2 units) or more overflows, which shows as a
+      // non-finite normaliser.  Then the whole workgroup runs the piece again
+      // with the per-tile bound and lazy rescale (the loop has drained: its
+      // last slot waited for every tile load and ended with a barrier).
+      pipeline(std::false_type{});
+      bool bad = false;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) bad |= !(l_fin[g] < INFINITY);
+      if (__syncthreads_or(bad)) pipeline(std::true_type{});
+    } else {
+      pipeline(std::true_type{});
+    }
 
     if (!SPLIT || (t_beg == 0 && t_end == n_all)) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float l_tot = sum_with_partner32(l_run[g]);
+        const float l_tot = l_fin[g];
         if (my_q[g] < Nq) {
           // This block's partial: O_b = acc / l_tot, LSE_b = m_ref + log2 l_tot
           // (log2 units).  MERGE folds it into the running (Out, LSE) of the row
@@ -718,7 +785,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       float lse_own[NG];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float l_tot = sum_with_partner32(l_run[g]);
+        const float l_tot = l_fin[g];
         lse_own[g] = m_ref[g] + fast_log2(l_tot);
         const float inv = 1.f / l_tot;
 #pragma unroll

@@ -114,16 +114,42 @@ def v9_slot_table():
     return [[(w >> (4 * i)) & 15 for i in range(9)] for w in words]
 
 
+def ones_skew():
+    m = re.search(r"constexpr int kOnesSkew = (\d+);", source())
+    assert m
+    return int(m.group(1))
+
+
 @pytest.mark.parametrize("D", HEAD_DIMS)
 def test_operand_reads_stay_in_buffer(D):
     """K operand reads (row kt * 32 + l32, unit (2c + hi) ^ swz mod kOct) and
     the transposing V reads (rows 4 (q / 2) + i / 4 of each 8-key half chunk,
     units 4 dt + 2 (q % 2) + (i % 4) / 2, swizzled) of a 64-key tile, every
-    chunk: all inside the tile plus its 16-unit slack."""
+    chunk: all inside the tile plus its 16-unit slack.  When d is not a
+    multiple of 32, the reads of units past the row (padding rows of O^T) go
+    to the ones region after the four buffers; from either V buffer they must
+    land inside it."""
     kBc = constant("kBc")
     kOct = D // 8
     kTileUnits = kBc * kOct
     kBufUnits = kTileUnits + 16
+    ones_row = D % 32 != 0
+    assert ("constexpr bool kOnesRow = (D % 32) != 0;" in source())
+    ones_units = kBufUnits + ones_skew() + 56 * kOct + 1 if ones_row else 0
+    for vbuf in (0, 1):                       # V buffers sit at units (2 + vbuf) * kBufUnits
+        base = (2 + vbuf) * kBufUnits
+        for lane in range(64):
+            q, i = lane >> 4, lane & 15
+            for dt in range((D + 31) // 32):
+                u = 4 * dt + 2 * (q & 1) + ((i & 3) >> 1)
+                if not (ones_row and u >= kOct):
+                    continue
+                for ch in range(kBc // 16):
+                    for up in (0, 8):
+                        first = base * 8 + (2 * kBufUnits + ones_skew()) * 8 + 4 * (i & 1) \
+                            + (16 * ch + up) * kOct * 8
+                        assert 4 * kBufUnits * 8 <= first
+                        assert first + 3 < (4 * kBufUnits + ones_units) * 8, (D, vbuf, lane, dt, ch)
     kChunks = (D + 15) // 16
     kDTiles = (D + 31) // 32
     kCH = kBc // 16
@@ -140,8 +166,10 @@ def test_operand_reads_stay_in_buffer(D):
         v_row = 4 * (q >> 1) + (i >> 2)
         for dt in range(kDTiles):
             u = 4 * dt + 2 * (q & 1) + ((i & 3) >> 1)
+            if ones_row and u >= kOct:
+                continue                      # checked above: the ones region
             if kOct == 9:
-                slot = v9[v_row & 3][min(u, 8)]
+                slot = v9[v_row & 3][u]
             elif kOct in (8, 16):
                 sv = 4 * (v_row & 3) if kOct == 16 else 4 * ((v_row >> 1) & 1)
                 slot = u ^ sv

@@ -275,6 +275,51 @@ def test_rescale_on_every_tile():
     assert_bf16_close(to_f64(l_acc), Lr, "rescale fused LSE")
 
 
+@pytest.mark.parametrize("d", [72, 40])
+@pytest.mark.parametrize("growth", [0.1, 1.0, 4.0])
+def test_ones_row_head_dims_fast_path_and_fallback(d, growth):
+    """Head dims that are not a multiple of 32 take the normaliser from the
+    PV product's padding rows and bound no weight per tile; a row whose
+    scores outgrow the first tile's maximum by 128 (log2 units) overflows
+    there and the workgroup reruns with the per-tile bound.  Scores rise by
+    about growth * d / 8 (natural units) per 64-key tile over 10 tiles:
+    0.1 stays near the first tile's maximum; 1.0 still runs on the fast path
+    with weights up to about 2^117 at d = 72, far above the exact path's
+    per-tile bound; 4.0 overflows within a few tiles and falls back.  Plain
+    launch, forced split and the fused merge over two blocks, against the
+    oracle."""
+    from attention_attn_block_amd import attn_block_workspace
+    B, H, Nq, Nkv = 1, 40, 200, 640
+    g = torch.Generator().manual_seed(int(100 * growth) + d)
+    tile = (torch.arange(Nkv) // 64).float()
+    k = (growth * tile)[None, None, :, None] + 0.3 * torch.randn(B, H, Nkv, d, generator=g)
+    q = 1.0 + 0.05 * torch.randn(B, H, Nq, d, generator=g)
+    v = torch.randn(B, H, Nkv, d, generator=g)
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    scale = 0.125
+    Or, Lr = oracle.ref_attn(to_oracle(q), to_oracle(k), to_oracle(v), scale)
+    gq, gk, gv = dev(q), dev(k), dev(v)
+    say("case ones-row head dim", d, "growth", growth)
+    O, L = attn_block_fwd(gq, gk, gv, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_f64(O), Or, f"d{d} growth {growth} plain O")
+    assert_bf16_close(to_f64(L), Lr, f"d{d} growth {growth} plain LSE")
+    ws = attn_block_workspace(gq, gk)
+    O, L = attn_block_fwd(gq, gk, gv, scale=scale, out_dtype=torch.float32, workspace=ws,
+                          force_split=True)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_f64(O), Or, f"d{d} growth {growth} split O")
+    assert_bf16_close(to_f64(L), Lr, f"d{d} growth {growth} split LSE")
+    o_acc = torch.zeros(B, H, Nq, d, dtype=torch.float32, device="cuda:0")
+    l_acc = torch.full((B, H, Nq), float("-inf"), dtype=torch.float32, device="cuda:0")
+    for lo, hi in ((0, 320), (320, Nkv)):
+        attn_block_fwd_merge(gq, gk[:, :, lo:hi].contiguous(), gv[:, :, lo:hi].contiguous(), o_acc,
+                             l_acc, scale=scale)
+    torch.cuda.synchronize()
+    assert_bf16_close(to_f64(o_acc), Or, f"d{d} growth {growth} fused O")
+    assert_bf16_close(to_f64(l_acc), Lr, f"d{d} growth {growth} fused LSE")
+
+
 @pytest.mark.parametrize("Nkv", [30, 100, 1000])
 def test_ragged_tile_ignores_stale_lds(Nkv):
     """Key rows past a ragged last tile must not carry over whatever an earlier
