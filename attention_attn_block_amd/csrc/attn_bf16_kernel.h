@@ -456,15 +456,18 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     bf16x8 pb[NG][kCH];
 
     // W(t): scores of tile t (raw, in s_nxt) -> weights pb, normaliser share.
-    // kSafe = false (ones-row head dims only): the weights alone; the
-    // normaliser comes out of the PV product and nothing bounds the weights
-    // per tile (checked once after the key loop).
-    auto w_phase = [&](auto safe_c, int t) __attribute__((always_inline)) {
+    // kSafe = false, the fast path: nothing bounds the weights per tile (a
+    // non-finite normaliser after the key loop sends the piece to the exact
+    // path); with the ones row the normaliser comes out of the PV product
+    // and the phase computes the weights alone.  kFirst: tile 0, which sets
+    // the reference max.
+    auto w_phase = [&](auto safe_c, auto first_c, int t) __attribute__((always_inline)) {
       constexpr bool kSafe = decltype(safe_c)::value;
+      constexpr bool kFirst = decltype(first_c)::value;
       mask_tail(s_nxt, kvb + t * kBc);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        if (t == 0) {  // reference max from tile 0
+        if constexpr (kFirst) {  // reference max from tile 0
           l_run[g] = 0.f;
           m_ref[g] = max_with_partner32(row_max(s_nxt[g])) * c2;
         }
@@ -474,7 +477,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 #pragma unroll
           for (int r = 0; r < 16; ++r) s_nxt[g][kt][r] = fmaf(s_nxt[g][kt][r], c2, neg_m);
       }
-      if constexpr (!kSafe) {
+      if constexpr (!kSafe && kOnesRow) {
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -514,7 +517,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       bool any_big = false;
 #pragma unroll
       for (int g = 0; g < NG; ++g) any_big |= !(ls[g] <= kLaneSumLimit);
-      if (__builtin_amdgcn_ballot_w64(any_big)) {
+      if (kSafe && __builtin_amdgcn_ballot_w64(any_big)) {
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           const float mx = max_with_partner32(row_max(s_nxt[g]));
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     // wave must have finished those reads first.
     __syncthreads();
 
-    w_phase(safe_c, 0);
+    w_phase(safe_c, std::true_type{}, 0);
 
     // One slot; p = slot index mod 4 (compile-time), so the buffer of every
     // tile a slot touches is known: in slots 4j + {0, 1} tile k is even, in
@@ -643,12 +646,12 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
         if (grp == 0) {
           if (k < n_tiles) m_phase(KQ{}, KP{}, k);
         } else {
-          if (k >= 1 && k < n_tiles) w_phase(safe_c, k);
+          if (k >= 1 && k < n_tiles) w_phase(safe_c, std::false_type{}, k);
         }
       } else {
         if (grp == 0) {  // group A is in its vector phase in odd slots
           if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], kvb + (k + 1) * kBc);
-          if (k + 1 < n_tiles) w_phase(safe_c, k + 1);
+          if (k + 1 < n_tiles) w_phase(safe_c, std::false_type{}, k + 1);
         } else {
           if (k < n_tiles) m_phase(KQ{}, KP{}, k);
         }
@@ -678,24 +681,21 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      l_fin[g] = kSafe ? sum_with_partner32(l_run[g]) : acc[g][G::kDTiles - 1][kOnesElt];
+      l_fin[g] = (kSafe || !kOnesRow) ? sum_with_partner32(l_run[g])
+                                      : acc[g][G::kDTiles - 1][kOnesElt];
     };  // pipeline
 
-    if constexpr (kOnesRow) {
-      // Fast path first.  Its weights are exp2 of (score - reference max of
-      // the first tile) with no bound: a row whose scores later outgrow that
-      // reference by 128 (log2 units) or more overflows, which shows as a
-      // non-finite normaliser.  Then the whole workgroup runs the piece again
-      // with the per-tile bound and lazy rescale (the loop has drained: its
-      // last slot waited for every tile load and ended with a barrier).
-      pipeline(std::false_type{});
-      bool bad = false;
+    // Fast path first.  Its weights are exp2 of (score - reference max of the
+    // first tile) with no per-tile bound: a row whose scores later outgrow
+    // that reference by 128 (log2 units) or more overflows, which shows as a
+    // non-finite normaliser.  Then the whole workgroup runs the piece again
+    // with the per-tile bound and lazy rescale (the loop has drained: its
+    // last slot waited for every tile load and ended with a barrier).
+    pipeline(std::false_type{});
+    bool bad = false;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) bad |= !(l_fin[g] < INFINITY);
-      if (__syncthreads_or(bad)) pipeline(std::true_type{});
-    } else {
-      pipeline(std::true_type{});
-    }
+    for (int g = 0; g < NG; ++g) bad |= !(l_fin[g] < INFINITY);
+    if (__syncthreads_or(bad)) pipeline(std::true_type{});
 
     if (!SPLIT || (t_beg == 0 && t_end == n_all)) {
 #pragma unroll
