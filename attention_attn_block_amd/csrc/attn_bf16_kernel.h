@@ -429,6 +429,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 
     f32x16 acc[NG][G::kDTiles];
     float l_run[NG];   // this lane's share of each row's normaliser (bf16 weights)
+    float l_ch[NG][4];  // the same on the fast path, as four running dot chains
     float m_ref[NG];   // reference row max for the exponentials, log2 units
     float l_fin[NG];   // each row's normaliser at the end of the key loop
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
@@ -469,6 +470,8 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       for (int g = 0; g < NG; ++g) {
         if constexpr (kFirst) {  // reference max from tile 0
           l_run[g] = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) l_ch[g][c] = 0.f;
           m_ref[g] = max_with_partner32(row_max(s_nxt[g])) * c2;
         }
         const float neg_m = -m_ref[g];
@@ -477,14 +480,25 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 #pragma unroll
           for (int r = 0; r < 16; ++r) s_nxt[g][kt][r] = fmaf(s_nxt[g][kt][r], c2, neg_m);
       }
-      if constexpr (!kSafe && kOnesRow) {
+      if constexpr (!kSafe) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
+        for (int g = 0; g < NG; ++g) {
 #pragma unroll
           for (int ch = 0; ch < kCH; ++ch)
 #pragma unroll
             for (int j = 0; j < 8; ++j)
               pb[g][ch][j] = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
+          if constexpr (!kOnesRow) {
+            // The normaliser sums the same bf16 weights the product uses, in
+            // four chains that run on across tiles (no per-tile total).
+#pragma unroll
+            for (int ch = 0; ch < kCH; ++ch)
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                l_ch[g][c] = __builtin_amdgcn_fdot2_f32_bf16(
+                    bf16x2{pb[g][ch][2 * c], pb[g][ch][2 * c + 1]}, ones, l_ch[g][c], false);
+          }
+        }
         return;
       }
       float ls[NG];
@@ -681,8 +695,9 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g)
-      l_fin[g] = (kSafe || !kOnesRow) ? sum_with_partner32(l_run[g])
-                                      : acc[g][G::kDTiles - 1][kOnesElt];
+      l_fin[g] = kSafe      ? sum_with_partner32(l_run[g])
+                 : kOnesRow ? acc[g][G::kDTiles - 1][kOnesElt]
+                            : sum_with_partner32((l_ch[g][0] + l_ch[g][1]) + (l_ch[g][2] + l_ch[g][3]));
     };  // pipeline
 
     // Fast path first.  Its weights are exp2 of (score - reference max of the
