@@ -380,12 +380,9 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       for (int c = 0; c < G::kChunks; ++c) {
 #pragma unroll
         for (int kt = 0; kt < kKT; ++kt) {
-          bf16x8 a;
-          if (G::kHalfTail && c == G::kChunks - 1 && hi) {
-            a = bf16x8{};
-          } else {
-            a = __builtin_bit_cast(bf16x8, k_lds[buf][kt * 32 * G::kOct + k_unit[c]]);
-          }
+          // In a half-filled last chunk the upper half-wave's K operand holds
+          // another unit of the same row (finite data): its Q operand is zero.
+          const bf16x8 a = __builtin_bit_cast(bf16x8, k_lds[buf][kt * 32 * G::kOct + k_unit[c]]);
 #pragma unroll
           for (int g = 0; g < NG; ++g) s[g][kt] = mfma32(a, qf[g][c], s[g][kt]);
         }
@@ -576,7 +573,6 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
         bf16x8 kr[kQK];
         auto kread = [&](int i) -> bf16x8 {
           const int c = i / kKT, kt = i % kKT;
-          if (G::kHalfTail && c == G::kChunks - 1 && hi) return bf16x8{};
           return __builtin_bit_cast(bf16x8, k_lds[kb][kt * 32 * G::kOct + k_unit[c]]);
         };
 #pragma unroll

@@ -54,14 +54,15 @@ def v_pass_words(kOct, slot, dt, row0):
 
 
 def k_pass_words(kOct, slot, kt, c, half_tail):
+    """K operand reads: lane (l32, hi) reads unit slot(row, 2c + hi) mod kOct
+    of row kt * 32 + l32.  In a half-filled last chunk (half_tail) the upper
+    half-wave's unit index wraps to a real unit of the row (its Q operand is
+    zero), so every lane reads."""
     words = []
     for lane in range(64):
         l32, hi = lane & 31, lane >> 5
-        if half_tail and hi:
-            words.append([])
-            continue
         row = kt * 32 + l32
-        base = (row * kOct + slot(row, 2 * c + hi)) * 4                # 16-byte unit -> 4 words
+        base = (row * kOct + slot(row, 2 * c + hi) % kOct) * 4         # 16-byte unit -> 4 words
         words.append([base, base + 1, base + 2, base + 3])
     return words
 
