@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     attn_lse_merge,
     attn_patch_fwd,
     attn_patch_fwd_strided,
+    attn_ring_fwd,
     cfg_combine,
     cfg_combine_relmae,
     default_scale,

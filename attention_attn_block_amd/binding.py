@@ -19,7 +19,7 @@ DIT_F32, DIT_BF16 = 0, 1
 
 EXPORTS = ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws",
            "attn_block_workspace_bytes", "attn_lse_merge", "attn_patch_fwd", "attn_patch_fwd_ws",
-           "attn_patch_fwd_strided",
+           "attn_patch_fwd_strided", "attn_ring_fwd",
            "cfg_combine", "cfg_combine_relmae", "cfg_combine_relmae_noalloc",
            "cfg_combine_relmae_workspace", "dit_status_string")
 
@@ -54,13 +54,15 @@ def load():
                                     vp]
     L.attn_patch_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i,
                                          i, vp, ll, vp]
+    L.attn_ring_fwd.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, f, i, i, i, vp, ll, vp]
     L.cfg_combine.argtypes = [vp, vp, vp, ll, f, vp]
     L.cfg_combine_relmae.argtypes = [vp, vp, vp, ll, f, vp, vp, vp]
     L.cfg_combine_relmae_noalloc.argtypes = [vp, vp, vp, ll, f, vp, vp]
     L.cfg_combine_relmae_workspace.argtypes = [ll]
     L.cfg_combine_relmae_workspace.restype = ll
     for name in ("attn_block_fwd", "attn_block_fwd_merge", "attn_block_fwd_ws", "attn_lse_merge",
-                 "attn_patch_fwd", "attn_patch_fwd_ws", "attn_patch_fwd_strided", "cfg_combine",
+                 "attn_patch_fwd", "attn_patch_fwd_ws", "attn_patch_fwd_strided", "attn_ring_fwd",
+                 "cfg_combine",
                  "cfg_combine_relmae",
                  "cfg_combine_relmae_noalloc"):
         getattr(L, name).restype = ctypes.c_int
@@ -296,6 +298,48 @@ def attn_patch_fwd_strided(q_p, k_p, v_p, k_buf, v_buf, p0, run_len, run_stride,
                                            N, int(p0), d, scale, _dtype(q_p.dtype),
                                            _dtype(out_dtype), ws_ptr, ws_bytes, _stream(dev))
     _check("attn_patch_fwd_strided", rc)
+    return out, lse
+
+
+def attn_ring_fwd(q, ks, vs, scale=None, out_dtype=None, out=None, lse=None, workspace=None,
+                  force_split=False):
+    """(O, LSE) = attention of q [B,H,Nq,d] against the concatenation of the
+    KV blocks ks[i], vs[i] ([B,H,Nkv_block,d] each, bfloat16, up to 16
+    blocks) in one launch.  workspace, force_split: as for attn_block_fwd."""
+    if len(ks) != len(vs) or not ks:
+        raise ValueError("ks and vs must be equally long, non-empty lists of blocks")
+    dev = _dev(q, *ks, *vs)
+    B, H, Nq, d = q.shape
+    Nkv = ks[0].shape[2]
+    for kb, vb in zip(ks, vs):
+        if kb.shape != (B, H, Nkv, d) or vb.shape != kb.shape or kb.dtype != q.dtype \
+                or vb.dtype != q.dtype:
+            raise ValueError("q and the KV blocks disagree in shape or dtype")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    _dev(q, out, lse)
+    if out.shape != (B, H, Nq, d) or out.dtype != out_dtype or lse.shape != (B, H, Nq) \
+            or lse.dtype != torch.float32:
+        raise ValueError("out/lse shape or dtype mismatch")
+    n = len(ks)
+    kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in ks])
+    vp_ = (ctypes.c_void_p * n)(*[t.data_ptr() for t in vs])
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev(q, workspace)
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor (attn_block_workspace)")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    with torch.cuda.device(dev):
+        rc = load().attn_ring_fwd(q.data_ptr(), kp, vp_, n, out.data_ptr(), lse.data_ptr(), B, H,
+                                  Nq, Nkv, d, scale, _dtype(q.dtype), _dtype(out_dtype),
+                                  WS_FORCE_SPLIT if force_split else 0, ws_ptr, ws_bytes,
+                                  _stream(dev))
+    _check("attn_ring_fwd", rc)
     return out, lse
 
 

@@ -14,6 +14,8 @@
 
 static_assert(DIT_RELMAE_NOALLOC_MAX_N == dit::kRelmaeStaticMaxN,
               "the header's limit must match the library's scratch array");
+static_assert(DIT_MAX_KV_BLOCKS == dit::kAttnMaxBlocks && DIT_MAX_BLOCK_KEYS == dit::kAttnMaxBlockKeys,
+              "the header's block-set limits must match the kernel's");
 
 namespace {
 
@@ -144,6 +146,58 @@ dit_status_t attn_block_fwd_ws(const void* Q, const void* K, const void* V, void
     if (overlaps(workspace, (size_t)need, all[i], allb[i])) return DIT_ERR_INVALID_ARG;
   return run_attn(Q, K, V, O_acc, LSE_acc, B * H, Nq, Nkv, d, scale, in_dtype, out_dtype,
                   (flags & DIT_WS_MERGE) != 0, workspace, (flags & DIT_WS_FORCE_SPLIT) != 0, stream);
+}
+
+dit_status_t attn_ring_fwd(const void* Q, const void* const* K_blocks,
+                          const void* const* V_blocks, int n_blocks, void* O, float* LSE, int B,
+                          int H, int Nq, int Nkv_block, int d, float scale, dit_dtype_t in_dtype,
+                          dit_dtype_t out_dtype, int flags, void* workspace,
+                          long long workspace_bytes, hipStream_t stream) {
+  if (!K_blocks || !V_blocks) return DIT_ERR_INVALID_ARG;
+  if (n_blocks < 1 || n_blocks > DIT_MAX_KV_BLOCKS) return DIT_ERR_INVALID_ARG;
+  for (int i = 0; i < n_blocks; ++i)
+    if (!K_blocks[i] || !V_blocks[i]) return DIT_ERR_INVALID_ARG;
+  size_t qb, kvb, ob, lb;
+  dit_status_t st = check_attn(Q, K_blocks[0], V_blocks[0], O, LSE, B, H, Nq, Nkv_block, d, scale,
+                               (int)in_dtype, (int)out_dtype, &qb, &kvb, &ob, &lb);
+  if (st != DIT_OK) return st;
+  for (int i = 1; i < n_blocks; ++i)
+    if (!aligned16(K_blocks[i]) || !aligned16(V_blocks[i])) return DIT_ERR_INVALID_ARG;
+  if (flags & ~DIT_WS_FORCE_SPLIT) return DIT_ERR_INVALID_ARG;
+  if (in_dtype != DIT_BF16) return DIT_ERR_UNSUPPORTED;
+  if (Nkv_block > dit::kAttnMaxBlockKeys) return DIT_ERR_UNSUPPORTED;
+  const long long keys = (long long)n_blocks * ((Nkv_block + dit::kAttnKeysPerTile - 1) /
+                                                dit::kAttnKeysPerTile) * dit::kAttnKeysPerTile;
+  if (keys > kMaxI32) return DIT_ERR_UNSUPPORTED;
+  // Outputs overlap nothing that is read: Q and every block.
+  if (overlaps(O, ob, LSE, lb) || overlaps(O, ob, Q, qb) || overlaps(LSE, lb, Q, qb))
+    return DIT_ERR_INVALID_ARG;
+  for (int i = 0; i < n_blocks; ++i) {
+    const void* kv[2] = {K_blocks[i], V_blocks[i]};
+    for (int j = 0; j < 2; ++j)
+      if (overlaps(O, ob, kv[j], kvb) || overlaps(LSE, lb, kv[j], kvb)) return DIT_ERR_INVALID_ARG;
+  }
+  if (workspace) {
+    const long long need = attn_block_workspace_bytes(B, H, Nq, Nkv_block, d);
+    if (workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+      return DIT_ERR_INVALID_ARG;
+    if (overlaps(workspace, (size_t)need, Q, qb) || overlaps(workspace, (size_t)need, O, ob) ||
+        overlaps(workspace, (size_t)need, LSE, lb))
+      return DIT_ERR_INVALID_ARG;
+    for (int i = 0; i < n_blocks; ++i)
+      if (overlaps(workspace, (size_t)need, K_blocks[i], kvb) ||
+          overlaps(workspace, (size_t)need, V_blocks[i], kvb))
+        return DIT_ERR_INVALID_ARG;
+  }
+  dit::KVBlocks blocks{};
+  blocks.n = n_blocks;
+  for (int i = 0; i < n_blocks; ++i) {
+    blocks.k[i] = K_blocks[i];
+    blocks.v[i] = V_blocks[i];
+  }
+  return from_hip(dit::launch_attn_bf16_blocks(Q, &blocks, O, LSE, B * H, Nq, Nkv_block, d, scale,
+                                               out_dtype == DIT_F32, workspace,
+                                               (flags & DIT_WS_FORCE_SPLIT) != 0, stream));
 }
 
 dit_status_t attn_lse_merge(void* O_a, float* LSE_a, const void* O_b, const float* LSE_b,

@@ -12,7 +12,7 @@ namespace dit {
 template <int D>
 hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH,
                          int Nq, int Nkv, float scale, bool out_f32, bool merge, int split_grid,
-                         void* ws, hipStream_t stream);
+                         void* ws, const KVBlocks* blocks, hipStream_t stream);
 
 int attn_split_grid(long long n_items, int Nkv, int n_cu, int min_key_tiles) {
   const int n_all = (Nkv + kAttnKeysPerTile - 1) / kAttnKeysPerTile;
@@ -55,16 +55,14 @@ int device_cus(hipStream_t stream) {
 }
 }  // namespace
 
-hipError_t launch_attn_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                            int BH, int Nq, int Nkv, int d, float scale, bool out_f32, bool merge,
-                            void* ws, bool force_split, hipStream_t stream) {
-  const long long n_items = (long long)BH * ((Nq + kAttnRowsPerTile - 1) / kAttnRowsPerTile);
-  const int split_grid =
-      ws ? attn_split_grid(n_items, Nkv, device_cus(stream), force_split ? 0 : kAttnSplitMinKeyTiles) : 0;
+namespace {
+hipError_t dispatch(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH, int Nq,
+                    int Nkv, int d, float scale, bool out_f32, bool merge, int split_grid, void* ws,
+                    const KVBlocks* blocks, hipStream_t stream) {
   switch (d) {
 #define DIT_CASE(DD) \
   case DD:           \
-    return launch_bf16_d<DD>(Q, K, V, O, LSE, BH, Nq, Nkv, scale, out_f32, merge, split_grid, ws, stream);
+    return launch_bf16_d<DD>(Q, K, V, O, LSE, BH, Nq, Nkv, scale, out_f32, merge, split_grid, ws, blocks, stream);
     DIT_CASE(8) DIT_CASE(16) DIT_CASE(24) DIT_CASE(32) DIT_CASE(40) DIT_CASE(48) DIT_CASE(56)
     DIT_CASE(64) DIT_CASE(72) DIT_CASE(80) DIT_CASE(88) DIT_CASE(96) DIT_CASE(104) DIT_CASE(112)
     DIT_CASE(120) DIT_CASE(128)
@@ -72,6 +70,34 @@ hipError_t launch_attn_bf16(const void* Q, const void* K, const void* V, void* O
     default:
       return hipErrorInvalidValue;
   }
+}
+}  // namespace
+
+hipError_t launch_attn_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int BH, int Nq, int Nkv, int d, float scale, bool out_f32, bool merge,
+                            void* ws, bool force_split, hipStream_t stream) {
+  const long long n_items = (long long)BH * ((Nq + kAttnRowsPerTile - 1) / kAttnRowsPerTile);
+  const int split_grid =
+      ws ? attn_split_grid(n_items, Nkv, device_cus(stream), force_split ? 0 : kAttnSplitMinKeyTiles) : 0;
+  return dispatch(Q, K, V, O, LSE, BH, Nq, Nkv, d, scale, out_f32, merge, split_grid, ws, nullptr,
+                  stream);
+}
+
+hipError_t launch_attn_bf16_blocks(const void* Q, const KVBlocks* blocks, void* O, float* LSE,
+                                   int BH, int Nq, int Nkv, int d, float scale, bool out_f32,
+                                   void* ws, bool force_split, hipStream_t stream) {
+  if (!blocks || blocks->n < 1 || blocks->n > kAttnMaxBlocks || Nkv > kAttnMaxBlockKeys)
+    return hipErrorInvalidValue;
+  const long long n_items = (long long)BH * ((Nq + kAttnRowsPerTile - 1) / kAttnRowsPerTile);
+  // The planner sees the concatenation: n blocks of whole key tiles each.
+  const long long tpb = (Nkv + kAttnKeysPerTile - 1) / kAttnKeysPerTile;
+  const long long keys = (long long)blocks->n * tpb * kAttnKeysPerTile;
+  if (keys > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int split_grid = ws ? attn_split_grid(n_items, (int)keys, device_cus(stream),
+                                              force_split ? 0 : kAttnSplitMinKeyTiles)
+                            : 0;
+  return dispatch(Q, nullptr, nullptr, O, LSE, BH, Nq, Nkv, d, scale, out_f32, false, split_grid,
+                  ws, blocks, stream);
 }
 
 }  // namespace dit

@@ -213,11 +213,18 @@ __device__ __forceinline__ float row_max(const f32x16* s) {
 // with its own partial (O, LSE); the partials of a tile are combined with the
 // log-sum-exp identity by whichever piece arrives last, through the caller's
 // workspace.
-template <int D, int NG, bool OUT_F32, bool MERGE, bool SPLIT>
+//
+// MULTI: the keys are the concatenation of n_blocks KV blocks of Nkv keys each,
+// held in separate buffers (blk): one launch for a whole ring step whose
+// blocks are resident.  Key tile t of the concatenation is local tile
+// t % tpb of block t / tpb (tpb = key tiles per block); the quotient is a
+// scalar multiply-high by div_magic = ceil(2^32 / tpb) (tpb >= 2), exact for
+// the sizes the launcher admits.  Without MULTI, K and V are one block.
+template <int D, int NG, bool OUT_F32, bool MERGE, bool SPLIT, bool MULTI>
 __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     void* __restrict__ Out, float* __restrict__ LSE, int Nq, int Nkv, int n_qtiles, float c2,
-    int n_items, char* __restrict__ ws) {
+    int n_items, char* __restrict__ ws, KVBlocks blk, int n_blocks, unsigned div_magic) {
   using G = Geo<D>;
   constexpr int kRowsWG = (kThreads / 64) * 32 * NG;  // query rows per workgroup
   // K and V tiles: kBc rows of kOct 16-byte units each, unit-swizzled (see
@@ -256,7 +263,8 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   const int slot = bid >> 3;
   const int per = nblk >> 3, rem = nblk & 7;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
-  const int n_all = (Nkv + kBc - 1) / kBc;  // key tiles of the block
+  const int tpb = (Nkv + kBc - 1) / kBc;               // key tiles of one block
+  const int n_all = MULTI ? n_blocks * tpb : tpb;      // key tiles of the whole key range
 
   // Work units are (query tile, key tile) pairs in query-tile-major order;
   // this workgroup owns units [u, u_end).  Unsplit: exactly one query tile.
@@ -350,6 +358,28 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     const __bf16* Qh = Q + (size_t)bh * Nq * D;
     const __bf16* Kh = K + (size_t)bh * Nkv * D;
     const __bf16* Vh = V + (size_t)bh * Nkv * D;
+    // Source of key tile t of the piece: the (batch, head) slice of its block
+    // and the tile's first key inside that block.
+    auto tile_block = [&](int t) -> int {
+      if constexpr (MULTI) {
+        const unsigned ta = (unsigned)(t_beg + t);
+        return tpb == 1 ? (int)ta : (int)__umulhi(ta, div_magic);
+      } else {
+        return 0;
+      }
+    };
+    auto tile_kv0 = [&](int t) -> int {
+      if constexpr (MULTI) return (t_beg + t - tile_block(t) * tpb) * kBc;
+      else return kvb + t * kBc;
+    };
+    auto tile_k = [&](int t) -> const __bf16* {
+      if constexpr (MULTI) return static_cast<const __bf16*>(blk.k[tile_block(t)]) + (size_t)bh * Nkv * D;
+      else return Kh;
+    };
+    auto tile_v = [&](int t) -> const __bf16* {
+      if constexpr (MULTI) return static_cast<const __bf16*>(blk.v[tile_block(t)]) + (size_t)bh * Nkv * D;
+      else return Vh;
+    };
 
     // Query rows of this lane, one per group; Q^T as the B operand: lane holds
     // Q[row][16c + 8hi .. +7].
@@ -462,7 +492,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     auto w_phase = [&](auto safe_c, auto first_c, int t) __attribute__((always_inline)) {
       constexpr bool kSafe = decltype(safe_c)::value;
       constexpr bool kFirst = decltype(first_c)::value;
-      mask_tail(s_nxt, kvb + t * kBc);
+      mask_tail(s_nxt, tile_kv0(t));
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if constexpr (kFirst) {  // reference max from tile 0
@@ -627,9 +657,9 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 #pragma unroll
       for (int t = 0; t < G::kDTiles; ++t) acc[g][t] = f32x16{};
     if (grp == 1) {
-      dma_tile(IsK{}, Kh, k_lds[0], kvb);
-      dma_tile(IsV{}, Vh, v_lds[0], kvb);
-      if (n_tiles > 1) dma_tile(IsK{}, Kh, k_lds[1], kvb + kBc);
+      dma_tile(IsK{}, tile_k(0), k_lds[0], tile_kv0(0));
+      dma_tile(IsV{}, tile_v(0), v_lds[0], tile_kv0(0));
+      if (n_tiles > 1) dma_tile(IsK{}, tile_k(1), k_lds[1], tile_kv0(1));
     }
     dma_wait();
     __syncthreads();
@@ -651,7 +681,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       const int k = s >> 1;
       if constexpr ((p & 1) == 0) {
         if (grp == 1) {  // group B is in its vector phase in even slots
-          if (k + 2 < n_tiles) dma_tile(IsK{}, Kh, k_lds[kpar], kvb + (k + 2) * kBc);
+          if (k + 2 < n_tiles) dma_tile(IsK{}, tile_k(k + 2), k_lds[kpar], tile_kv0(k + 2));
         }
         if (grp == 0) {
           if (k < n_tiles) m_phase(KQ{}, KP{}, k);
@@ -660,7 +690,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
         }
       } else {
         if (grp == 0) {  // group A is in its vector phase in odd slots
-          if (k + 1 < n_tiles) dma_tile(IsV{}, Vh, v_lds[kpar ^ 1], kvb + (k + 1) * kBc);
+          if (k + 1 < n_tiles) dma_tile(IsV{}, tile_v(k + 1), v_lds[kpar ^ 1], tile_kv0(k + 1));
           if (k + 1 < n_tiles) w_phase(safe_c, std::false_type{}, k + 1);
         } else {
           if (k < n_tiles) m_phase(KQ{}, KP{}, k);
@@ -995,11 +1025,13 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 // Launch for one head dim (explicitly instantiated in the attn_bf16_d*.hip
 // files so the instantiations compile in parallel).  split_grid > 0 selects
 // the SPLIT kernel on that many workgroups, with `ws` laid out as
-// attn_split_workspace_bytes describes (one record per query tile).
+// attn_split_workspace_bytes describes (one record per query tile).  A
+// non-null `blocks` selects the MULTI kernel over blocks->n blocks of Nkv
+// keys (K and V unused); merge is then not supported.
 template <int D>
 hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, float* LSE, int BH,
                          int Nq, int Nkv, float scale, bool out_f32, bool merge, int split_grid,
-                         void* ws, hipStream_t stream) {
+                         void* ws, const KVBlocks* blocks, hipStream_t stream) {
   constexpr int NG = kGroups;
   constexpr int kRowsWG = (kThreads / 64) * 32 * NG;
   static_assert(kRowsWG == kAttnRowsPerTile && kBc == kAttnKeysPerTile,
@@ -1011,18 +1043,32 @@ hipError_t launch_bf16_d(const void* Q, const void* K, const void* V, void* O, f
   const __bf16* k = static_cast<const __bf16*>(K);
   const __bf16* v = static_cast<const __bf16*>(V);
   using Kern = void (*)(const __bf16*, const __bf16*, const __bf16*, void*, float*, int, int, int,
-                        float, int, char*);
+                        float, int, char*, KVBlocks, int, unsigned);
   const bool split = split_grid > 0;
-  // [out_f32][merge][split]
+  const bool multi = blocks != nullptr;
+  if (multi && merge) return hipErrorInvalidValue;
+  // [out_f32][merge][split], then [out_f32][split] for the block sets
   static constexpr Kern kKernels[2][2][2] = {
-      {{attn_fwd_bf16_kernel<D, NG, false, false, false>, attn_fwd_bf16_kernel<D, NG, false, false, true>},
-       {attn_fwd_bf16_kernel<D, NG, false, true, false>, attn_fwd_bf16_kernel<D, NG, false, true, true>}},
-      {{attn_fwd_bf16_kernel<D, NG, true, false, false>, attn_fwd_bf16_kernel<D, NG, true, false, true>},
-       {attn_fwd_bf16_kernel<D, NG, true, true, false>, attn_fwd_bf16_kernel<D, NG, true, true, true>}}};
-  const Kern kern = kKernels[out_f32][merge][split];
+      {{attn_fwd_bf16_kernel<D, NG, false, false, false, false>, attn_fwd_bf16_kernel<D, NG, false, false, true, false>},
+       {attn_fwd_bf16_kernel<D, NG, false, true, false, false>, attn_fwd_bf16_kernel<D, NG, false, true, true, false>}},
+      {{attn_fwd_bf16_kernel<D, NG, true, false, false, false>, attn_fwd_bf16_kernel<D, NG, true, false, true, false>},
+       {attn_fwd_bf16_kernel<D, NG, true, true, false, false>, attn_fwd_bf16_kernel<D, NG, true, true, true, false>}}};
+  static constexpr Kern kMulti[2][2] = {
+      {attn_fwd_bf16_kernel<D, NG, false, false, false, true>, attn_fwd_bf16_kernel<D, NG, false, false, true, true>},
+      {attn_fwd_bf16_kernel<D, NG, true, false, false, true>, attn_fwd_bf16_kernel<D, NG, true, false, true, true>}};
+  const Kern kern = multi ? kMulti[out_f32][split] : kKernels[out_f32][merge][split];
+  KVBlocks blk{};
+  int n_blocks = 1;
+  unsigned magic = 0;
+  if (multi) {
+    blk = *blocks;
+    n_blocks = blocks->n;
+    const unsigned tpb = (unsigned)((Nkv + kBc - 1) / kBc);
+    magic = tpb > 1 ? (unsigned)(((1ull << 32) + tpb - 1) / tpb) : 0u;  // ceil(2^32 / tpb)
+  }
   const dim3 grid((unsigned)(split ? split_grid : n_items));
   kern<<<grid, kThreads, 0, stream>>>(q, k, v, O, LSE, Nq, Nkv, n_qtiles, c2, n_items,
-                                      split ? static_cast<char*>(ws) : nullptr);
+                                      split ? static_cast<char*>(ws) : nullptr, blk, n_blocks, magic);
   return hipGetLastError();
 }
 

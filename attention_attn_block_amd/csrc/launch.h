@@ -39,6 +39,19 @@ int attn_split_grid(long long n_items, int Nkv, int n_cu, int min_key_tiles);
 // 2048-key block cannot hide; from 6144 keys the split is 9-22% faster).
 constexpr int kAttnSplitMinKeyTiles = 96;
 
+// The KV blocks of one ring step, resident on the device: block i's K and V
+// are [B, H, Nkv, d] buffers of their own.  Passed to the kernel by value.
+constexpr int kAttnMaxBlocks = 16;
+struct KVBlocks {
+  const void* k[kAttnMaxBlocks];
+  const void* v[kAttnMaxBlocks];
+  int n;
+};
+// Keys per block of a block set, at most: keeps the kernel's scalar division
+// of a key-tile index by the tiles per block exact (tile index x tiles per
+// block < 2^32).
+constexpr int kAttnMaxBlockKeys = 1 << 20;
+
 // Attention with bfloat16 Q/K/V (matrix cores), fp32 or bf16 output.  With
 // `merge`, (O, LSE) hold a running partial that the block's result is folded
 // into (LSE = -inf: empty) instead of being overwritten.  A non-null `ws`
@@ -48,6 +61,12 @@ constexpr int kAttnSplitMinKeyTiles = 96;
 hipError_t launch_attn_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                             int BH, int Nq, int Nkv, int d, float scale, bool out_f32, bool merge,
                             void* ws, bool force_split, hipStream_t stream);
+
+// The same over the concatenation of a block set (blocks->n blocks of Nkv
+// keys each, at most kAttnMaxBlockKeys), in one launch; no merge.
+hipError_t launch_attn_bf16_blocks(const void* Q, const KVBlocks* blocks, void* O, float* LSE,
+                                   int BH, int Nq, int Nkv, int d, float scale, bool out_f32,
+                                   void* ws, bool force_split, hipStream_t stream);
 
 // Attention with float32 Q/K/V/O (vector ALU, no reduced-precision products);
 // `merge` as for launch_attn_bf16.

@@ -396,12 +396,13 @@ def main():
 
 def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):
     """Reported beside the step: merge and CFG on cold HBM (rotating buffers
-    larger than the 256 MB Infinity Cache), the fused ring step, a long block
-    with few query tiles (plain grid vs split launch), and the d=72
-    workloads."""
+    larger than the 256 MB Infinity Cache), the fused ring step, the ring
+    share in one launch over its resident blocks, a long block with few query
+    tiles (plain grid vs split launch), the Ulysses and P = 8 PipeFusion
+    shares, and the d=72 workloads."""
     from attention_attn_block_amd import (attn_block_fwd, attn_block_fwd_merge, attn_block_workspace,
-                                          attn_lse_merge, attn_patch_fwd, cfg_combine,
-                                          cfg_combine_relmae)
+                                          attn_lse_merge, attn_patch_fwd, attn_ring_fwd,
+                                          cfg_combine, cfg_combine_relmae)
     res = {}
 
     def timed(fn, iters):
@@ -457,6 +458,23 @@ def supplementary(torch, dev, inputs, q_r, ks, vs, ring_scale):
     f = len(ks) * attn_flops(B, H, Nq, ks[0].shape[2], dd)
     res["ring_share_fused_merge"] = {"us_per_share": us, "tflops": f / (us * 1e-6) / 1e12,
                                      "frac_bf16_peak": f / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+
+    # The whole ring share in one launch over the 8 resident blocks
+    # (attn_ring_fwd): plain grid, and the library's choice with a workspace
+    # (256 key tiles per query tile: split).
+    wsr = attn_block_workspace(q_r, ks[0])
+    row = {}
+    for tag, kw in (("plain", {}), ("split", {"workspace": wsr})):
+        fn = lambda i: attn_ring_fwd(q_r, ks, vs, scale=ring_scale, out=o_acc, lse=l_acc,
+                                     out_dtype=torch.float32, **kw)
+        for i in range(10):
+            fn(i)
+        us = timed(fn, 20)
+        row[f"{tag}_us_per_share"] = us
+        row[f"{tag}_tflops"] = f / (us * 1e-6) / 1e12
+        row[f"{tag}_frac_bf16_peak"] = f / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+    res["ring_share_one_launch"] = row
+    del wsr
 
     # Few query tiles against a long block: 20 heads x 2048 queries (160 tiles
     # of 256 rows on 256 CUs) x 16384 keys, plain grid vs the split launch

@@ -157,6 +157,39 @@ dit_status_t attn_block_fwd_ws(const void* Q, const void* K, const void* V,
                                hipStream_t stream);
 
 /*
+ * One device's share of a Ring or Torus attention step in one launch: the
+ * queries against the concatenation of every KV block of the step, with the
+ * blocks resident on the device in buffers of their own (SwiftFusion,
+ * sections 1-2: the device folds every block's partial into its output;
+ * blocks over disjoint keys combine in any grouping).  The result is
+ * attention over all n_blocks * Nkv_block keys, the same as attn_block_fwd
+ * per block folded with attn_lse_merge, up to rounding, without writing or
+ * re-reading any block partial and with one launch's fixed cost instead of
+ * n_blocks.  A query tile's key range runs across the blocks in order; with
+ * a workspace the range may be shared between workgroups as for
+ * attn_block_fwd_ws.
+ *   Q: [B,H,Nq,d] bfloat16 (read only)
+ *   K_blocks, V_blocks: HOST arrays of n_blocks device pointers, each a
+ *     [B,H,Nkv_block,d] bfloat16 buffer (read only; blocks may repeat)
+ *   O: [B,H,Nq,d] out_dtype; LSE: [B,H,Nq] float32 (written)
+ *   1 <= n_blocks <= DIT_MAX_KV_BLOCKS; 1 <= Nkv_block <= DIT_MAX_BLOCK_KEYS;
+ *   flags: 0 or DIT_WS_FORCE_SPLIT; workspace: NULL (one workgroup per query
+ *   tile) or as for attn_block_fwd_ws.
+ * Returns DIT_ERR_UNSUPPORTED for float32 inputs (use attn_block_fwd_merge per
+ * block) and for Nkv_block above the limit; otherwise as attn_block_fwd_ws.
+ * O and LSE must not overlap Q, any block or the workspace.
+ */
+#define DIT_MAX_KV_BLOCKS 16
+#define DIT_MAX_BLOCK_KEYS (1 << 20)
+dit_status_t attn_ring_fwd(const void* Q, const void* const* K_blocks,
+                           const void* const* V_blocks, int n_blocks,
+                           void* O, float* LSE,
+                           int B, int H, int Nq, int Nkv_block, int d, float scale,
+                           dit_dtype_t in_dtype, dit_dtype_t out_dtype, int flags,
+                           void* workspace, long long workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * Log-sum-exp merge of two partials over disjoint key sets, in place into a.
  *
  * Per row r (rows = B*H*Nq):

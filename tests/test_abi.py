@@ -202,6 +202,70 @@ def test_attn_patch_fwd_strided_edge_layouts_pass_validation(lib):
 
 
 # ---------------------------------------------------------------------------
+# attn_ring_fwd (a ring step's resident KV blocks in one launch)
+# ---------------------------------------------------------------------------
+
+def ring(lib, **kw):
+    a = dict(Q=ptr(0), O=ptr(1), L=ptr(2), n=8, B=1, H=24, Nq=2048, Nkv=2048, d=128, scale=0.088,
+             i=BF16, o=F32, flags=0, W=None, nbytes=0, ks=None, vs=None)
+    a.update(kw)
+    n = a["n"]
+    ks = a["ks"] if a["ks"] is not None else [ptr(3 + j) for j in range(max(n, 0))]
+    vs = a["vs"] if a["vs"] is not None else [ptr(20 + j) for j in range(max(n, 0))]
+    karr = (ctypes.c_void_p * max(len(ks), 1))(*ks) if ks else None
+    varr = (ctypes.c_void_p * max(len(vs), 1))(*vs) if vs else None
+    return lib.attn_ring_fwd(a["Q"], karr, varr, n, a["O"], a["L"], a["B"], a["H"], a["Nq"],
+                             a["Nkv"], a["d"], a["scale"], a["i"], a["o"], a["flags"], a["W"],
+                             a["nbytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), INV), (dict(O=None), INV), (dict(L=None), INV),
+    (dict(n=0, ks=[], vs=[]), INV), (dict(n=17), INV),
+    (dict(ks=[ptr(3)] * 7 + [None]), INV),            # a null block
+    (dict(vs=[ptr(20)] * 7 + [ptr(27, 8)]), INV),      # a misaligned block
+    (dict(B=0), INV), (dict(Nkv=0), INV), (dict(scale=-1.0), INV), (dict(d=60), UNS),
+    (dict(i=F32, o=F32), UNS),                         # fp32 inputs: per-block calls instead
+    (dict(Nkv=(1 << 20) + 1), UNS),                    # past the block-length limit
+    (dict(flags=1), INV), (dict(flags=4), INV),        # merge flag or unknown flags
+    (dict(O=ptr(0, 64)), INV),                         # output overlaps Q
+    (dict(O=ptr(9)), INV),                             # output is K block 6
+    (dict(L=ptr(25, 128)), INV),                       # LSE inside V block 5
+    (dict(W=ptr(30)), INV),                            # workspace of 0 bytes
+    (dict(W=ptr(30, 16), nbytes=192 * SPLIT_RECORD_BYTES), INV),   # misaligned workspace
+    (dict(W=ptr(4), nbytes=192 * SPLIT_RECORD_BYTES), INV),        # workspace is K block 1
+])
+def test_attn_ring_fwd_rejects(lib, kw, code):
+    assert ring(lib, **kw) == code
+
+
+def test_attn_ring_fwd_accepts_repeated_blocks(lib):
+    """Blocks are read only, so the same block may appear more than once; a
+    valid call gets past the checks to the HIP runtime (DIT_ERR_HIP here,
+    without a GPU)."""
+    assert ring(lib, ks=[ptr(3)] * 8, vs=[ptr(20)] * 8) == HIP
+    assert ring(lib, n=16, Nkv=64) == HIP
+    assert ring(lib, W=ptr(40), nbytes=192 * SPLIT_RECORD_BYTES, flags=2) == HIP
+
+
+def test_block_division_is_exact():
+    """The kernel finds the block of key tile t of a block set as
+    mulhi(t, ceil(2^32 / tpb)) (tpb >= 2 tiles per block); exact for every
+    tile index of up to 16 blocks of up to 2^20 keys (the ABI's limits)."""
+    import random
+    rng = random.Random(5)
+    sizes = list(range(2, 200)) + [1 << 14, (1 << 14) - 1, 4096, 8191] + \
+        [rng.randrange(2, (1 << 14) + 1) for _ in range(200)]
+    for tpb in sizes:
+        m = ((1 << 32) + tpb - 1) // tpb
+        n_all = 16 * tpb
+        probes = set(range(min(n_all, 3000))) | {n_all - 1, n_all - 2, n_all // 2}
+        probes |= {rng.randrange(n_all) for _ in range(500)}
+        for t in probes:
+            assert (t * m) >> 32 == t // tpb, (tpb, t)
+
+
+# ---------------------------------------------------------------------------
 # cfg_combine
 # ---------------------------------------------------------------------------
 
