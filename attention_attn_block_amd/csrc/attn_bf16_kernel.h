@@ -347,9 +347,13 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 
   while (u < u_end) {
     // One piece: key tiles [t_beg, t_end) of query tile `item`.
-    const int item = (int)(u / n_all);
-    const int t_beg = (int)(u - (long long)item * n_all);
-    const int t_end = (int)(u_end - u < (long long)(n_all - t_beg) ? t_beg + (u_end - u) : n_all);
+    // The piece's indices are the same in every lane; the compiler computes
+    // the 64-bit division in vector registers, so they are made scalar here
+    // once (everything derived from them then stays in scalar registers).
+    const int item = __builtin_amdgcn_readfirstlane((int)(u / n_all));
+    const int t_beg = __builtin_amdgcn_readfirstlane((int)(u - (long long)item * n_all));
+    const int t_end = __builtin_amdgcn_readfirstlane(
+        (int)(u_end - u < (long long)(n_all - t_beg) ? t_beg + (u_end - u) : n_all));
     u += t_end - t_beg;
     const int bh = item / n_qtiles;
     const int qt = item - bh * n_qtiles;
@@ -360,16 +364,19 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     const __bf16* Vh = V + (size_t)bh * Nkv * D;
     // Source of key tile t of the piece: the (batch, head) slice of its block
     // and the tile's first key inside that block.
+    // (The tile index is wave-uniform; readfirstlane keeps the block lookup
+    // and the tile's buffer resource in scalar registers.)
     auto tile_block = [&](int t) -> int {
       if constexpr (MULTI) {
-        const unsigned ta = (unsigned)(t_beg + t);
+        const unsigned ta = (unsigned)__builtin_amdgcn_readfirstlane(t_beg + t);
         return tpb == 1 ? (int)ta : (int)__umulhi(ta, div_magic);
       } else {
         return 0;
       }
     };
     auto tile_kv0 = [&](int t) -> int {
-      if constexpr (MULTI) return (t_beg + t - tile_block(t) * tpb) * kBc;
+      if constexpr (MULTI)
+        return (__builtin_amdgcn_readfirstlane(t_beg + t) - tile_block(t) * tpb) * kBc;
       else return kvb + t * kBc;
     };
     auto tile_k = [&](int t) -> const __bf16* {
