@@ -51,9 +51,13 @@
 //    pipeline.
 // Scores are kept in the log2 domain (scale * log2 e folded into one FMA) and
 // exponentiated with v_exp_f32; the LSE is converted back to natural log.
-// P is rounded to bfloat16 (RNE, v_cvt_pk_bf16_f32) for the PV product and
-// the normaliser sums those same bf16 weights (v_dot2_f32_bf16 against ones),
-// so the output is an exactly normalised combination of the values.
+// P is rounded to bfloat16 (RNE, v_cvt_pk_bf16_f32) for the PV product.  The
+// normaliser is the fp32 sum of the fp32 weights before that rounding, added
+// with ordinary v_add_f32: on gfx950 the dot instructions (v_dot2_f32_bf16)
+// issue to the matrix pipe, so a wave waiting on one stalls its whole vector
+// phase behind the other wave's MFMAs.  When d is not a multiple of 32 the
+// fast path instead takes the normaliser from padding rows of the PV product
+// (the sum of the bf16 weights; see kOnesRow).
 
 #pragma once
 
@@ -69,7 +73,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // padding rows of O^T (d pads to 32 kDTiles); the transposing V reads of
   // those rows are pointed at a region of bf16 ones, so each padding row of
   // O^T accumulates the row sum of the weights: the normaliser comes out of
-  // the matrix cores, and the vector phase needs no sums (see kFastNorm).
+  // the matrix cores, and the fast vector phase needs no sums (see w_phase).
   // The region lies past the four tile buffers and is sized so that the
   // address of every padding read -- a fixed offset of two buffers plus
   // kOnesSkew units from either V buffer, plus the chunk and half-chunk
@@ -466,7 +469,6 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     float l_ch[NG][4];  // the same on the fast path, as four running dot chains
     float m_ref[NG];   // reference row max for the exponentials, log2 units
     float l_fin[NG];   // each row's normaliser at the end of the key loop
-    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
     const int n_tiles = t_end - t_beg;  // key tiles of this piece
     // Accumulator element of a lane that holds a padding row of O^T (row
     // 32 (kDTiles - 1) + 8 (e / 4) + 4 hi + e % 4 >= d for both half-waves).
@@ -491,6 +493,8 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     bf16x8 pb[NG][kCH];
 
     // W(t): scores of tile t (raw, in s_nxt) -> weights pb, normaliser share.
+    // The normaliser adds the fp32 weights before their rounding to bf16, in
+    // plain adds (no dot instructions: those wait for the matrix pipe).
     // kSafe = false, the fast path: nothing bounds the weights per tile (a
     // non-finite normaliser after the key loop sends the piece to the exact
     // path); with the ones row the normaliser comes out of the PV product
@@ -516,46 +520,37 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
       }
       if constexpr (!kSafe) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
+        for (int g = 0; g < NG; ++g)
 #pragma unroll
           for (int ch = 0; ch < kCH; ++ch)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-              pb[g][ch][j] = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
-          if constexpr (!kOnesRow) {
-            // The normaliser sums the same bf16 weights the product uses, in
-            // four chains that run on across tiles (no per-tile total).
-#pragma unroll
-            for (int ch = 0; ch < kCH; ++ch)
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                l_ch[g][c] = __builtin_amdgcn_fdot2_f32_bf16(
-                    bf16x2{pb[g][ch][2 * c], pb[g][ch][2 * c + 1]}, ones, l_ch[g][c], false);
-          }
-        }
+            for (int j = 0; j < 8; j += 2) {
+              const float e0 = fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
+              const float e1 = fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j + 1]);
+              pb[g][ch][j] = (__bf16)e0;
+              pb[g][ch][j + 1] = (__bf16)e1;
+              // Four chains that run on across tiles (no per-tile total).
+              if constexpr (!kOnesRow) l_ch[g][j >> 1] += e0 + e1;
+            }
         return;
       }
       float ls[NG];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
+        // This lane's share of the tile's normaliser also bounds every weight
+        // the lane holds.  Four independent chains.
+        float lc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ch = 0; ch < kCH; ++ch)
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            pb[g][ch][j] = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
-        // The normaliser sums the same bf16 weights the product uses; this
-        // lane's share of it also bounds every weight the lane holds.  Four
-        // independent accumulation chains keep the dot unit's latency off the
-        // vector phase.
-        float ls0 = 0.f, ls1 = 0.f, ls2 = 0.f, ls3 = 0.f;
-#pragma unroll
-        for (int ch = 0; ch < kCH; ++ch) {
-          ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][0], pb[g][ch][1]}, ones, ls0, false);
-          ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][2], pb[g][ch][3]}, ones, ls1, false);
-          ls2 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][4], pb[g][ch][5]}, ones, ls2, false);
-          ls3 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][6], pb[g][ch][7]}, ones, ls3, false);
-        }
-        ls[g] = (ls0 + ls1) + (ls2 + ls3);
+          for (int j = 0; j < 8; j += 2) {
+            const float e0 = fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j]);
+            const float e1 = fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j + 1]);
+            pb[g][ch][j] = (__bf16)e0;
+            pb[g][ch][j + 1] = (__bf16)e1;
+            lc[j >> 1] += e0 + e1;
+          }
+        ls[g] = (lc[0] + lc[1]) + (lc[2] + lc[3]);
       }
       // Rare: a lane's share of a row's sum exceeds the limit (so some weight
       // there exceeds 2^9), i.e. the row's scores grew well past its reference
@@ -578,20 +573,20 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[g][dt][r] *= alpha;
           m_ref[g] += delta;
-          float ls0 = 0.f, ls1 = 0.f;
+          // Recompute the tile's weights against the moved reference (a row
+          // that did not grow has delta = 0 and gets the same weights back).
+          float lc0 = 0.f, lc1 = 0.f;
 #pragma unroll
-          for (int ch = 0; ch < kCH; ++ch) {
+          for (int ch = 0; ch < kCH; ++ch)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const __bf16 re = (__bf16)fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j] - delta);
-              pb[g][ch][j] = grow ? re : pb[g][ch][j];
+            for (int j = 0; j < 8; j += 2) {
+              const float e0 = fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j] - delta);
+              const float e1 = fast_exp2(s_nxt[g][ch >> 1][8 * (ch & 1) + j + 1] - delta);
+              pb[g][ch][j] = (__bf16)e0;
+              pb[g][ch][j + 1] = (__bf16)e1;
+              if (j & 2) lc1 += e0 + e1; else lc0 += e0 + e1;
             }
-            ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][0], pb[g][ch][1]}, ones, ls0, false);
-            ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][2], pb[g][ch][3]}, ones, ls1, false);
-            ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][4], pb[g][ch][5]}, ones, ls0, false);
-            ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[g][ch][6], pb[g][ch][7]}, ones, ls1, false);
-          }
-          ls[g] = ls0 + ls1;
+          ls[g] = lc0 + lc1;
         }
       }
 #pragma unroll
