@@ -245,6 +245,9 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // offsets -- lands in it.  The skew moves the padding reads to other banks
   // than the real V reads of the same pass (none conflict at d = 72).
   constexpr bool kOnesRow = (D % 32) != 0;
+  // fp32 output at d = 128 (a ring step's block partials) leaves through LDS
+  // in whole lines; see the epilogue.
+  constexpr bool kStagedOut = OUT_F32 && !MERGE && !SPLIT && D == 128 && NG == 1;
   constexpr int kOnesSkew = 8;
   constexpr int kOnesUnits = kOnesRow ? kBufUnits + kOnesSkew + 56 * G::kOct + 1 : 0;
   __shared__ u32x4 lds_all[4 * kBufUnits + kOnesUnits];
@@ -771,7 +774,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
           }
           const size_t orow = lrow * D;
 #pragma unroll
-          for (int dt = 0; dt < G::kDTiles; ++dt)
+          for (int dt = 0; dt < (kStagedOut ? 0 : G::kDTiles); ++dt)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
               const int d0 = dt * 32 + 8 * q4 + 4 * hi;
@@ -799,6 +802,45 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
               }
             }
           if (hi == 0) LSE[lrow] = lse_new * kLn2;
+        }
+      }
+      if constexpr (kStagedOut) {
+        // Written straight from the accumulators, each store would cover 32-byte
+        // pieces of 32 rows (two lanes per row), 32 cache-line requests per
+        // instruction.  Instead each wave passes its rows through its own 8 KB
+        // slice of the tile buffers (idle since the key loop's last barrier),
+        // two 32-column tiles at a time, and every store then writes whole
+        // 128-byte lines of 4 rows.  Unit u (16 bytes) of slice row r sits at
+        // u ^ (r % 16): each 16-lane pass of the writes and of the reads meets
+        // 16 different units.
+        static_assert(kThreads / 64 * 512 <= 4 * kBufUnits, "staging slices fit the tile buffers");
+        u32x4* slice = lds_all + wave * 512;
+        const float wb0 = 1.f / l_fin[0];
+        const int q_base = qt * kRowsWG + wave * 32;
+        float* out_rows = static_cast<float*>(Out) + ((size_t)bh * Nq + q_base) * D;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int u = dd * 8 + 2 * q4 + hi;
+              const f32x16& a = acc[0][2 * h + dd];
+              slice[l32 * 16 + (u ^ (l32 & 15))] = __builtin_bit_cast(
+                  u32x4, f32x4{a[4 * q4] * wb0, a[4 * q4 + 1] * wb0, a[4 * q4 + 2] * wb0,
+                               a[4 * q4 + 3] * wb0});
+            }
+          // The reads take other lanes' writes: wave-ordered LDS, made visible
+          // to the compiler by the clobber.
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+          for (int it = 0; it < 8; ++it) {
+            const int r = it * 4 + (lane >> 4), c = lane & 15;
+            const u32x4 v4 = slice[r * 16 + (c ^ (r & 15))];
+            if (q_base + r < Nq)
+              *reinterpret_cast<u32x4*>(out_rows + (size_t)r * D + h * 64 + c * 4) = v4;
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // before the slice is rewritten
         }
       }
     } else {

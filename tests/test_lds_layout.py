@@ -128,3 +128,52 @@ def test_d128_xor_swizzles_conflict_free(kind):
         sw = lambda r, u: u ^ (4 * (r & 3))
         for dt in range(4):
             assert extra_cycles(v_pass_words(16, sw, dt, 0), 32) == 0
+
+
+def test_staged_fp32_output_layout():
+    """The fp32 epilogue at d = 128 passes each wave's 32 rows through an 8 KB
+    LDS slice, two 32-column tiles (64 columns, 16 units of 16 bytes) at a
+    time: lane (l32, hi) writes unit u = 8 dd + 2 q4 + hi (columns 4u..4u+3 of
+    the half) of row l32 at slot l32 * 16 + (u ^ (l32 % 16)); read pass it,
+    lane L takes unit c = L % 16 of row r = 4 it + L / 16 from slot
+    r * 16 + (c ^ (r % 16)) and stores it to global memory.  Checked: the
+    writes fill the slice once, every read gets row r's columns 4c..4c+3,
+    neither side meets a bank twice in a 16-lane pass, each store instruction
+    covers whole 128-byte lines, and the eight slices fit the tile buffers."""
+    txt = open(SRC).read()
+    assert "slice[l32 * 16 + (u ^ (l32 & 15))]" in txt
+    assert "slice[r * 16 + (c ^ (r & 15))]" in txt
+    assert "const int u = dd * 8 + 2 * q4 + hi;" in txt
+    assert "const int r = it * 4 + (lane >> 4), c = lane & 15;" in txt
+    assert 8 * 512 <= 4 * (64 * 16 + 16)
+    holds = {}
+    for lane in range(64):
+        l32, hi = lane & 31, lane >> 5
+        for dd in range(2):
+            for q4 in range(4):
+                u = dd * 8 + 2 * q4 + hi
+                slot = l32 * 16 + (u ^ (l32 & 15))
+                assert slot not in holds
+                holds[slot] = (l32, 4 * u)
+    assert sorted(holds) == list(range(512))
+    # one write instruction per (dd, q4): 16-byte stores, 16 lanes per pass
+    for dd in range(2):
+        for q4 in range(4):
+            words = []
+            for lane in range(64):
+                l32, hi = lane & 31, lane >> 5
+                u = dd * 8 + 2 * q4 + hi
+                s = l32 * 16 + (u ^ (l32 & 15))
+                words.append([4 * s + k for k in range(4)])
+            assert extra_cycles(words, 16) == 0, (dd, q4)
+    for it in range(8):
+        words, lines = [], set()
+        for lane in range(64):
+            r, c = it * 4 + (lane >> 4), lane & 15
+            s = r * 16 + (c ^ (r & 15))
+            assert holds[s] == (r, 4 * c)
+            words.append([4 * s + k for k in range(4)])
+            byte = r * 128 * 4 + 4 * c * 4            # global offset inside the half, row stride 512 B
+            lines.add(byte // 128)
+        assert extra_cycles(words, 16) == 0, it
+        assert len(lines) == 8                         # 64 lanes x 16 B = 8 whole lines
