@@ -248,6 +248,8 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
   // fp32 output at d = 128 (a ring step's block partials) leaves through LDS
   // in whole lines; see the epilogue.
   constexpr bool kStagedOut = OUT_F32 && !MERGE && !SPLIT && D == 128 && NG == 1;
+  // bf16 output at d = 72 likewise, through a linear copy of the wave's rows.
+  constexpr bool kStagedBf16 = !OUT_F32 && !MERGE && !SPLIT && D == 72 && NG == 1;
   constexpr int kOnesSkew = 8;
   constexpr int kOnesUnits = kOnesRow ? kBufUnits + kOnesSkew + 56 * G::kOct + 1 : 0;
   __shared__ u32x4 lds_all[4 * kBufUnits + kOnesUnits];
@@ -748,6 +750,7 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
     if (__syncthreads_or(bad)) pipeline(std::true_type{});
 
     if (!SPLIT || (t_beg == 0 && t_end == n_all)) {
+      float st_wb = 0.f;  // the staged bf16 epilogue's row weight (NG = 1)
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const float l_tot = l_fin[g];
@@ -773,8 +776,9 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
             }
           }
           const size_t orow = lrow * D;
+          st_wb = wb;
 #pragma unroll
-          for (int dt = 0; dt < (kStagedOut ? 0 : G::kDTiles); ++dt)
+          for (int dt = 0; dt < (kStagedOut || kStagedBf16 ? 0 : G::kDTiles); ++dt)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
               const int d0 = dt * 32 + 8 * q4 + 4 * hi;
@@ -841,6 +845,42 @@ __global__ __launch_bounds__(kThreads, NG == 1 ? kWavesPerSimd : 1) void attn_fw
               *reinterpret_cast<u32x4*>(out_rows + (size_t)r * D + h * 64 + c * 4) = v4;
           }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // before the slice is rewritten
+        }
+      }
+      if constexpr (kStagedBf16) {
+        // The wave's 32 rows are one contiguous range of Out (32 * D bf16).
+        // Stored from the accumulators, each store would cover 16-byte pieces
+        // of 32 rows.  Instead the lanes' 8-byte pieces go to a linear copy of
+        // that range in the wave's own part of the (idle) tile buffers, and
+        // the wave then copies it out in consecutive 16-byte units, whole
+        // lines per store.  A row's 144 bytes are 9 whole units.
+        static_assert((kThreads / 64) * 32 * D * 2 <= 4 * kBufUnits * 16, "copies fit the tile buffers");
+        static_assert((D * 2) % 16 == 0, "a unit never straddles two rows");
+        char* slice = reinterpret_cast<char*>(lds_all) + wave * (32 * D * 2);
+#pragma unroll
+        for (int dt = 0; dt < G::kDTiles; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = dt * 32 + 8 * q4 + 4 * hi;
+            if (d0 < D) {
+              const f32x16& a = acc[0][dt];
+              *reinterpret_cast<bf16x4*>(slice + (l32 * D + d0) * 2) =
+                  bf16x4{(__bf16)(a[4 * q4] * st_wb), (__bf16)(a[4 * q4 + 1] * st_wb),
+                         (__bf16)(a[4 * q4 + 2] * st_wb), (__bf16)(a[4 * q4 + 3] * st_wb)};
+            }
+          }
+        // The reads take other lanes' writes: wave-ordered LDS, made visible
+        // to the compiler by the clobber.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        constexpr int kUnits = 32 * D * 2 / 16;
+        const int q_base = qt * kRowsWG + wave * 32;
+        __bf16* out_base = static_cast<__bf16*>(Out) + ((size_t)bh * Nq + q_base) * D;
+#pragma unroll
+        for (int k = 0; k < (kUnits + 63) / 64; ++k) {
+          const int unit = k * 64 + lane;
+          if (unit < kUnits && q_base + unit / (D / 8) < Nq)
+            *reinterpret_cast<u32x4*>(out_base + unit * 8) =
+                *reinterpret_cast<const u32x4*>(slice + unit * 16);
         }
       }
     } else {

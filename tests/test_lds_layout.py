@@ -177,3 +177,35 @@ def test_staged_fp32_output_layout():
             lines.add(byte // 128)
         assert extra_cycles(words, 16) == 0, it
         assert len(lines) == 8                         # 64 lanes x 16 B = 8 whole lines
+
+
+def test_staged_bf16_output_layout_d72():
+    """The bf16 epilogue at d = 72 writes each lane's pieces (4 bf16 at
+    columns d0 = 32 dt + 8 q4 + 4 hi < 72 of row l32) into a linear copy of
+    the wave's 32 output rows and then copies that out in 16-byte units.
+    Checked: the pieces cover every row's 72 columns exactly once, a unit
+    never straddles two rows (row = unit / 9), the units cover the copy once,
+    and eight copies fit the four tile buffers."""
+    txt = open(SRC).read()
+    assert "slice + (l32 * D + d0) * 2" in txt
+    assert "q_base + unit / (D / 8) < Nq" in txt
+    D, k_dtiles = 72, 3
+    cover = {}
+    for lane in range(64):
+        l32, hi = lane & 31, lane >> 5
+        for dt in range(k_dtiles):
+            for q4 in range(4):
+                d0 = dt * 32 + 8 * q4 + 4 * hi
+                if d0 < D:
+                    for e in range(4):
+                        key = (l32, d0 + e)
+                        assert key not in cover
+                        cover[key] = (l32 * D + d0 + e) * 2
+    assert sorted(cover) == [(r, c) for r in range(32) for c in range(D)]
+    assert sorted(cover.values()) == list(range(0, 32 * D * 2, 2))   # a linear copy
+    units = 32 * D * 2 // 16
+    for unit in range(units):
+        first, last = unit * 16 // 2, unit * 16 // 2 + 7                # bf16 elements
+        assert first // D == last // D == unit // (D // 8)
+    k_buf_units = 64 * (D // 8) + 16
+    assert 8 * 32 * D * 2 <= 4 * k_buf_units * 16
